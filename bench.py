@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the lightning-indexer logits library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--hot]
+                    [--no-cpu] [--only IDX] [--calib-copy MB]
+
+A step is one call of the op over one batch of synthetic input (every stage of
+the kernel: Q/weights prologue, K load or block-table gather, fp8 MFMA,
+relu.weight epilogue, lane-permute head reduce, kv-scale, masked store and
+-inf fill).  The headline line is paged decode, batch 16, next_n 6, context
+131072, 64-token blocks (the workload the pages' own decode timings are quoted
+on); the other four named workloads are measured in the same run and reported
+under "workloads".
+
+Timing: W eager warm-up calls, then exactly K calls captured in one HIP graph
+and replayed once between two events on the launch stream, with
+synchronisation on both sides.  Inputs rotate over enough copies that the
+working set exceeds the 256 MB MALL (cold, as a serving step sees per-layer
+KV); --hot keeps one copy.
+
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_TBS = 8.0
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA (no sparsity)
+COLD_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="headline workload index")
+    ap.add_argument("--only", type=int, default=None, help="measure just this workload")
+    ap.add_argument("--hot", action="store_true", help="one input copy (MALL-warm)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+class Workload:
+    """Device-resident input copies and output buffers for one named workload."""
+
+    def __init__(self, idx, hot):
+        import torch
+        from sparse_attention_indexer_scaled_amd import inputs, workload
+        self.idx = idx
+        self.cfg = inputs.CONFIGS[idx]
+        self.kind = self.cfg["kind"]
+        t0 = time.time()
+        host = inputs.make_config(idx)
+        self.gen_s = time.time() - t0
+        self.host = host
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        if self.kind == "prefill":
+            base = dict(q=dev(host.q), k=dev(host.k), sc=dev(host.kv_scale), w=dev(host.weights),
+                        ks=dev(host.ks), ke=dev(host.ke))
+            self.out_shape = (host.M, host.N)
+            self.bytes = workload.prefill_essential_bytes(host.M, host.N)
+            self.pairs = workload.prefill_valid_pairs(host.ks, host.ke, host.N)
+            set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + host.M * host.N * 4
+        else:
+            base = dict(q=dev(host.q), cache=dev(host.kv_cache), w=dev(host.weights),
+                        ctx=dev(host.context_lens), bt=dev(host.block_tables))
+            self.out_shape = (host.B * host.next_n, host.max_model_len)
+            self.bytes = workload.decode_essential_bytes(host.B, host.next_n, host.context_lens,
+                                                         host.max_model_len)
+            self.pairs = workload.decode_valid_pairs(host.next_n, host.context_lens,
+                                                     host.max_model_len)
+            set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
+                self.out_shape[0] * self.out_shape[1] * 4
+        self.flops = self.pairs * workload.flops_per_pair()
+        nsets = 1 if hot else min(64, max(1, -(-COLD_BYTES // set_bytes)))
+        self.sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        self.outs = [torch.empty(self.out_shape, dtype=torch.float32, device="cuda")
+                     for _ in range(nsets)]
+        self.nsets = nsets
+
+    def call(self, i):
+        from sparse_attention_indexer_scaled_amd import mqa_logits_prefill, paged_mqa_logits_decode
+        s = self.sets[i % self.nsets]
+        out = self.outs[i % self.nsets]
+        if self.kind == "prefill":
+            mqa_logits_prefill(s["q"], s["k"], s["sc"], s["w"], s["ks"], s["ke"], logits=out)
+        else:
+            paged_mqa_logits_decode(s["q"], s["cache"], s["w"], s["ctx"], s["bt"],
+                                    self.host.max_model_len, logits=out)
+
+
+def time_workload(wl, steps, warmup, graph=True):
+    import torch
+    for i in range(warmup):
+        wl.call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(steps):
+                    wl.call(i)
+        stream.wait_stream(side)
+        g.replay()  # one untimed replay so the graph itself is resident
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if graph:
+        g.replay()
+    else:
+        for i in range(steps):
+            wl.call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    return ms / steps
+
+
+def summarize(wl, ms):
+    us = ms * 1e3
+    d = dict(workload=wl.cfg["name"], us_per_call=round(us, 3), input_copies=wl.nsets,
+             essential_bytes=int(wl.bytes), valid_pairs=int(wl.pairs))
+    tbs = wl.bytes / (ms * 1e-3) / 1e12
+    tflops = wl.flops / (ms * 1e-3) / 1e12
+    d["essential_TBps"] = round(tbs, 4)
+    d["hbm_frac"] = round(tbs / HBM_PEAK_TBS, 4)
+    d["fp8_TFLOPs"] = round(tflops, 2)
+    d["mfma_frac"] = round(tflops / FP8_PEAK_TFLOPS, 4)
+    return d
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle on a bounded sample of the headline decode workload: whole
+    sequences, one after another, until about budget_s of wall time is spent."""
+    import oracle
+    from sparse_attention_indexer_scaled_amd import workload
+    h = wl.host
+    nthreads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    oracle.set_num_threads(nthreads)
+    done, t0 = [], time.time()
+    for b in range(h.B):
+        oracle.decode(h.q[b:b + 1], h.kv_cache, h.weights[b * h.next_n:(b + 1) * h.next_n],
+                      h.context_lens[b:b + 1], h.block_tables[b:b + 1], h.max_model_len, h.block_size)
+        done.append(b)
+        if time.time() - t0 > budget_s:
+            break
+    dt = time.time() - t0
+    ctx = h.context_lens[done]
+    nbytes = workload.decode_essential_bytes(len(done), h.next_n, ctx, h.max_model_len)
+    return {"value": round(nbytes / dt / 1e12, 8), "unit": "TB/s", "cores": nthreads,
+            "kind": "oracle", "cpu": cpu_model(), "seconds": round(dt, 2),
+            "sample": "%d of %d sequences (all %d rows each, every position to max_model_len) of %s"
+                      % (len(done), h.B, h.next_n, wl.cfg["name"])}
+
+
+def calib_copy(mib):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "reads": n, "writes": n}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the op needs no exchange between GPUs; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "needs a HIP device"
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from sparse_attention_indexer_scaled_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        from sparse_attention_indexer_scaled_amd import build
+        build.build()
+    _native.load_library()
+    if args.calib_copy:
+        calib_copy(args.calib_copy)
+        return
+
+    order = [args.only] if args.only is not None else [args.workload] + \
+        [i for i in (1, 4, 3, 0) if i != args.workload]
+    results, head = {}, None
+    for idx in order:
+        wl = Workload(idx, args.hot)
+        ms = time_workload(wl, args.steps, args.warmup, graph=not args.no_graph)
+        results[wl.cfg["name"]] = summarize(wl, ms)
+        print("[bench] %s: %.2f us/call" % (wl.cfg["name"], ms * 1e3), file=sys.stderr, flush=True)
+        if idx == order[0]:
+            head = (wl, ms)
+        else:
+            del wl
+            torch.cuda.empty_cache()
+
+    wl, ms = head
+    r = results[wl.cfg["name"]]
+    h = wl.host
+    decode = wl.kind == "decode"
+    line = {
+        "metric": "decode essential HBM TB/s (% of 8 TB/s); prefill fp8 TFLOP/s; us/call",
+        "value": r["essential_TBps"] if decode else r["fp8_TFLOPs"],
+        "unit": "TB/s" if decode else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; N(0,1) Q/K, per-token fp8 K scale, random block table)",
+        "config": ({"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
+                    "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
+                    "heads": 32, "head_dim": 128, "kv_block_size": 64, "cold": not args.hot}
+                   if decode else
+                   {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": 32, "head_dim": 128,
+                    "cold": not args.hot}),
+        "roofline": ({"bound": "hbm", "achieved": round(r["essential_TBps"] * 1e3, 2),
+                      "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s", "frac": r["hbm_frac"],
+                      "traffic": None} if decode else
+                     {"bound": "mfma", "achieved": r["fp8_TFLOPs"], "peak": FP8_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": r["mfma_frac"], "traffic": None}),
+        "workloads": results,
+    }
+    if not args.no_cpu and decode:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

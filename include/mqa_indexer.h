@@ -1,0 +1,160 @@
+/*
+ * mqa_indexer.h -- C ABI of the MI355X (gfx950) lightning-indexer logits library
+ * (libmqa_indexer.so).
+ *
+ * The op (aiter PR 5047 page and aiter PR 5046 page, section "Motivation"):
+ *
+ *   logits[m, n] = sum_h relu(<Q[m,h,:], K[n,:]>) * kv_scale[n] * weights[m,h]
+ *
+ * for n inside row m's window and -inf elsewhere, with Q and K in fp8 e4m3fn
+ * (OCP E4M3, finite-only), a per-token fp32 K dequant scale, 32 heads and head
+ * dim 128.
+ *
+ * Conventions shared by every call:
+ *   - All array arguments are DEVICE pointers owned by the caller, contiguous,
+ *     row-major, on the current HIP device.  fp8 arrays are passed as raw
+ *     bytes (uint8_t).  Data pointers must be 16-byte aligned, int32 arrays
+ *     4-byte aligned.
+ *   - The library allocates no device memory and keeps no state between calls
+ *     except the per-thread last-error string.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).  A
+ *     call returns before the kernel finishes; outputs are valid once the
+ *     stream has been synchronised.
+ *   - Return value: MQA_OK (0) or a negative MQA_ERR_* code; on error nothing is
+ *     enqueued and mqa_last_error() describes why.  No call aborts the process
+ *     and no call falls back to another implementation.
+ *   - Integer arrays that live on the device (context_lens, block_tables,
+ *     cu_seqlen_ks/ke) cannot be inspected without a synchronisation, so their
+ *     documented ranges are preconditions, not checked.  Windows are clamped
+ *     into the output row, so no window value can make the kernel write
+ *     outside `logits`.
+ */
+#ifndef MQA_INDEXER_H
+#define MQA_INDEXER_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MQA_OK 0
+#define MQA_ERR_INVALID_ARG (-1) /* NULL/misaligned pointer, bad size, bad tunable */
+#define MQA_ERR_UNSUPPORTED (-2) /* shape or device outside mqa_is_supported()    */
+#define MQA_ERR_LAUNCH (-3)      /* the HIP runtime rejected the kernel launch     */
+#define MQA_ERR_DEVICE (-4)      /* no usable HIP device / device query failed     */
+
+/*
+ * Launch tunables.  0 in any field means "use the host heuristic"; every
+ * override changes only how the work is split, never a result bit (outputs are
+ * bitwise identical across all valid overrides).  Pass NULL for all-heuristic.
+ * (Both pages, "Technical Details": the row block, the column / KV split and
+ * the wave count are host-chosen and overridable.)
+ *
+ *   prefill:
+ *     block_m      query rows that share one K stream per wave: 1, 2, 4 or 8
+ *     split_n      workgroups per row block along the columns, >= 1
+ *     num_warps    waves per workgroup (they split the column range), 1..8
+ *     reverse_rows 1 = dispatch row blocks high-m first, -1 = natural order
+ *   decode:
+ *     rows_per_block  next_n rows that share one K stream per wave, 1..8
+ *                     (clamped to next_n)
+ *     split_kv        workgroups per (sequence, row group) along KV, >= 1
+ *     num_warps       as above
+ */
+typedef struct mqa_tunables {
+    int block_m;
+    int split_n;
+    int num_warps;
+    int reverse_rows;
+    int rows_per_block;
+    int split_kv;
+} mqa_tunables;
+
+/*
+ * Support gate (both pages, "Technical Details": the kernels are fixed to 32
+ * heads and head_dim 128 on gfx950, and callers route other shapes elsewhere
+ * instead of failing).  kv_block_size: 0 asks about prefill, 64 about paged
+ * decode with 64-token blocks.  Returns 1 if the current HIP device is gfx950
+ * and the shape is supported, else 0.  Never fails.
+ */
+int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
+
+/*
+ * Prefill logits over a contiguous, already-gathered K (aiter PR 5046 page,
+ * "Motivation" and "Technical Details").
+ *
+ *   q_fp8        [M, num_heads, head_dim]  fp8 e4m3fn
+ *   k_fp8        [N, head_dim]             fp8 e4m3fn
+ *   kv_scale     [N]                       fp32, >= 0
+ *   weights      [M, num_heads]            fp32
+ *   cu_seqlen_ks [M]                       int32
+ *   cu_seqlen_ke [M]                       int32
+ *   logits       [M, N]                    fp32, written
+ *
+ * Row m's window is  max(ks[m], 0) <= n < min(ke[m], N)  (empty when ke <= ks,
+ * when ke <= 0 or when ks >= N).  clean_logits != 0: every other column of the
+ * row is written -inf (the fused fill); clean_logits == 0: only the window is
+ * written and all other elements keep their previous contents.
+ * kv_scale must be >= 0 (the kernel applies it after the ReLU, once per column).
+ * M == 0 or N == 0 is a successful no-op.  M, N < 0, M*N beyond int64 range,
+ * NULL or misaligned pointers, or bad tunables -> MQA_ERR_INVALID_ARG; a shape
+ * outside the gate -> MQA_ERR_UNSUPPORTED.
+ */
+int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *kv_scale,
+                       const float *weights, const int32_t *cu_seqlen_ks,
+                       const int32_t *cu_seqlen_ke, float *logits, int M, int N, int num_heads,
+                       int head_dim, int clean_logits, const mqa_tunables *tun,
+                       hipStream_t stream);
+
+/*
+ * Paged decode logits (aiter PR 5047 page, "Motivation" and "Technical
+ * Details"; the next_n row bound is also spelled out on the issue page about
+ * next_n tiling, "The ask").
+ *
+ *   q_fp8        [batch, next_n, num_heads, head_dim]  fp8 e4m3fn
+ *   kv_cache     [num_blocks] blocks of kv_block_size * (head_dim + 4) bytes.
+ *                Block i starts at byte i * kv_block_size * (head_dim + 4); its
+ *                first kv_block_size * head_dim bytes are the fp8 K rows of
+ *                its slots (slot s at byte s * head_dim), the remaining
+ *                kv_block_size * 4 bytes the slots' fp32 dequant scales (slot
+ *                s at byte kv_block_size * head_dim + 4 s).  For 64-token
+ *                blocks a block is 8448 bytes, so every K row stays 16-byte
+ *                aligned.
+ *   weights      [batch * next_n, num_heads]  fp32
+ *   context_lens [batch]                      int32
+ *   block_tables [batch, max_blocks_per_seq]  int32; entry (b, i) is the
+ *                physical block holding positions [i*bs, (i+1)*bs) of
+ *                sequence b
+ *   logits       [batch * next_n, max_model_len]  fp32, written
+ *
+ * Row r = b * next_n + j covers positions 0 <= p <= context_lens[b] - next_n + j
+ * (none if that bound is negative).  clean_logits != 0 writes -inf at every
+ * other position p < max_model_len of the row; clean_logits == 0 writes only
+ * the window.
+ * Preconditions (not checked, see above): 0 <= context_lens[b] <=
+ * min(max_model_len, max_blocks_per_seq * kv_block_size); every table entry
+ * with index < ceil(context_lens[b] / kv_block_size) lies in [0, num_blocks).
+ * Entries past that are never read.  Scales must be >= 0.  Cache slots past a
+ * sequence's context may hold any bytes (NaN included): they never reach an
+ * output.
+ * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
+ * negative sizes, NULL or misaligned pointers -> MQA_ERR_INVALID_ARG; a shape
+ * or block size outside the gate -> MQA_ERR_UNSUPPORTED.
+ */
+int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *weights,
+                            const int32_t *context_lens, const int32_t *block_tables,
+                            float *logits, int batch, int next_n, int num_heads, int head_dim,
+                            int kv_block_size, int num_blocks, int max_blocks_per_seq,
+                            int max_model_len, int clean_logits, const mqa_tunables *tun,
+                            hipStream_t stream);
+
+/* Human-readable reason for this thread's last non-zero return ("" if none). */
+const char *mqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_INDEXER_H */

@@ -1,0 +1,166 @@
+"""ctypes binding of libmqa_indexer.so (include/mqa_indexer.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and the current HIP stream are handed to
+the C ABI.  Every step of the op runs in the library's HIP kernels; there is no
+other implementation behind these functions, and a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmqa_indexer.so")
+
+MQA_OK = 0
+MQA_ERR_INVALID_ARG = -1
+MQA_ERR_UNSUPPORTED = -2
+MQA_ERR_LAUNCH = -3
+MQA_ERR_DEVICE = -4
+
+EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode", "mqa_last_error")
+
+
+class MQAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class Tunables(ctypes.Structure):
+    """mqa_tunables: 0 in a field means the host heuristic chooses."""
+    _fields_ = [("block_m", ctypes.c_int), ("split_n", ctypes.c_int),
+                ("num_warps", ctypes.c_int), ("reverse_rows", ctypes.c_int),
+                ("rows_per_block", ctypes.c_int), ("split_kv", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MQAError(MQA_ERR_DEVICE, f"{path} is missing: build it with "
+                       "`python -m sparse_attention_indexer_scaled_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.mqa_is_supported.restype = I
+    lib.mqa_is_supported.argtypes = [I, I, I]
+    lib.mqa_last_error.restype = ctypes.c_char_p
+    lib.mqa_last_error.argtypes = []
+    lib.mqa_logits_prefill.restype = I
+    lib.mqa_logits_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P]
+    lib.paged_mqa_logits_decode.restype = I
+    lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P]
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().mqa_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != MQA_OK:
+        raise MQAError(rc, last_error())
+
+
+def is_supported(num_heads: int, head_dim: int, kv_block_size: int = 0) -> bool:
+    return bool(load_library().mqa_is_supported(int(num_heads), int(head_dim), int(kv_block_size)))
+
+
+def _bytes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be float8_e4m3fn or uint8 bytes, got {t.dtype}")
+    return t
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _tun(tunables: Optional[Tunables]):
+    return ctypes.byref(tunables) if tunables is not None else None
+
+
+def mqa_logits_prefill(q_fp8: torch.Tensor, k_fp8: torch.Tensor, kv_scale: torch.Tensor,
+                       weights: torch.Tensor, cu_seqlen_ks: torch.Tensor,
+                       cu_seqlen_ke: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                       clean_logits: bool = True, tunables: Optional[Tunables] = None,
+                       stream=None) -> torch.Tensor:
+    """q_fp8 [M,H,D], k_fp8 [N,D] (fp8 e4m3fn), kv_scale [N] f32, weights [M,H] f32,
+    cu_seqlen_ks/ke [M] int32 -> logits [M,N] f32 (allocated if not given)."""
+    q = _bytes(q_fp8, "q_fp8")
+    k = _bytes(k_fp8, "k_fp8")
+    M, H, D = q.shape
+    N = k.shape[0]
+    if k.shape != (N, D) or kv_scale.shape != (N,) or weights.shape != (M, H):
+        raise ValueError("shape mismatch")
+    if cu_seqlen_ks.shape != (M,) or cu_seqlen_ke.shape != (M,):
+        raise ValueError("cu_seqlen_ks/ke must be [M]")
+    if logits is None:
+        logits = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    if logits.shape != (M, N):
+        raise ValueError("logits must be [M, N]")
+    rc = load_library().mqa_logits_prefill(
+        _dev(q, "q_fp8"), _dev(k, "k_fp8"), _dev(kv_scale, "kv_scale", torch.float32),
+        _dev(weights, "weights", torch.float32), _dev(cu_seqlen_ks, "cu_seqlen_ks", torch.int32),
+        _dev(cu_seqlen_ke, "cu_seqlen_ke", torch.int32), _dev(logits, "logits", torch.float32),
+        M, N, H, D, int(bool(clean_logits)), _tun(tunables), _stream(stream, q.device))
+    _check(rc)
+    return logits
+
+
+def paged_mqa_logits_decode(q_fp8: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
+                            context_lens: torch.Tensor, block_tables: torch.Tensor,
+                            max_model_len: int, kv_block_size: int = 64,
+                            logits: Optional[torch.Tensor] = None, clean_logits: bool = True,
+                            tunables: Optional[Tunables] = None, stream=None) -> torch.Tensor:
+    """q_fp8 [B,next_n,H,D] fp8, kv_cache [num_blocks, bs*(D+4)] bytes, weights
+    [B*next_n,H] f32, context_lens [B] int32, block_tables [B,max_blocks] int32
+    -> logits [B*next_n, max_model_len] f32 (allocated if not given)."""
+    q = _bytes(q_fp8, "q_fp8")
+    cache = _bytes(kv_cache, "kv_cache")
+    B, next_n, H, D = q.shape
+    num_blocks = cache.shape[0]
+    if cache.dim() != 2 or cache.shape[1] != kv_block_size * (D + 4):
+        raise ValueError("kv_cache must be [num_blocks, kv_block_size*(head_dim+4)] bytes")
+    if weights.shape != (B * next_n, H) or context_lens.shape != (B,):
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks_per_seq]")
+    rows = B * next_n
+    if logits is None:
+        logits = torch.empty((rows, max_model_len), dtype=torch.float32, device=q.device)
+    if logits.shape != (rows, max_model_len):
+        raise ValueError("logits must be [B*next_n, max_model_len]")
+    rc = load_library().paged_mqa_logits_decode(
+        _dev(q, "q_fp8"), _dev(cache, "kv_cache"), _dev(weights, "weights", torch.float32),
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), _dev(logits, "logits", torch.float32),
+        B, next_n, H, D, int(kv_block_size), num_blocks, block_tables.shape[1], int(max_model_len),
+        int(bool(clean_logits)), _tun(tunables), _stream(stream, q.device))
+    _check(rc)
+    return logits

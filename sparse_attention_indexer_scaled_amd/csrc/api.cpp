@@ -1,0 +1,253 @@
+// C-ABI entry points: argument validation, the support gate, the host launch
+// heuristic and the per-thread error string.  Declared in include/mqa_indexer.h.
+#include "mqa_indexer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return MQA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// gfx950 check for the current device, cached per device id.
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices]; // 0 unknown, 1 gfx950, -1 other
+std::mutex g_arch_mu;
+
+int current_device_is_gfx950(int *dev_out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    if (dev_out)
+        *dev_out = dev;
+    if (dev < kMaxDevices && g_arch_ok[dev] != 0)
+        return g_arch_ok[dev] > 0 ? 1 : 0;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    const int is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    if (dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lk(g_arch_mu);
+        g_arch_ok[dev] = is950 ? 1 : -1;
+    }
+    return is950;
+}
+
+int check_device()
+{
+    int dev = -1;
+    const int r = current_device_is_gfx950(&dev);
+    if (r < 0)
+        return fail(MQA_ERR_DEVICE, "no usable HIP device");
+    if (r == 0)
+        return fail(MQA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return MQA_OK;
+}
+
+bool shape_supported(int num_heads, int head_dim, int kv_block_size)
+{
+    return num_heads == 32 && head_dim == 128 && (kv_block_size == 0 || kv_block_size == 64);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Optional one-line trace of the chosen launch (MQA_TRACE=1).
+bool trace_on()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("MQA_TRACE");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+} // namespace
+
+extern "C" int mqa_is_supported(int num_heads, int head_dim, int kv_block_size)
+{
+    if (!shape_supported(num_heads, head_dim, kv_block_size))
+        return 0;
+    return current_device_is_gfx950(nullptr) == 1 ? 1 : 0;
+}
+
+extern "C" const char *mqa_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *kv_scale,
+                                  const float *weights, const int32_t *cu_seqlen_ks,
+                                  const int32_t *cu_seqlen_ke, float *logits, int M, int N,
+                                  int num_heads, int head_dim, int clean_logits,
+                                  const mqa_tunables *tun, hipStream_t stream)
+{
+    if (M < 0 || N < 0)
+        return fail(MQA_ERR_INVALID_ARG, "M=%d, N=%d must be >= 0", M, N);
+    if (!shape_supported(num_heads, head_dim, 0))
+        return fail(MQA_ERR_UNSUPPORTED, "prefill supports num_heads=32, head_dim=128 (got %d, %d)",
+                    num_heads, head_dim);
+    mqa_tunables t = {};
+    if (tun)
+        t = *tun;
+    if (t.block_m != 0 && t.block_m != 1 && t.block_m != 2 && t.block_m != 4 && t.block_m != 8)
+        return fail(MQA_ERR_INVALID_ARG, "block_m must be 0, 1, 2, 4 or 8 (got %d)", t.block_m);
+    if (t.split_n < 0 || t.num_warps < 0 || t.num_warps > 4)
+        return fail(MQA_ERR_INVALID_ARG, "split_n >= 0 and num_warps in 0..4 required");
+    if (t.reverse_rows < -1 || t.reverse_rows > 1)
+        return fail(MQA_ERR_INVALID_ARG, "reverse_rows must be -1, 0 or 1");
+    if (M == 0 || N == 0)
+        return ok();
+    if (!q_fp8 || !k_fp8 || !kv_scale || !weights || !cu_seqlen_ks || !cu_seqlen_ke || !logits)
+        return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(q_fp8, 16) || !aligned(k_fp8, 16) || !aligned(kv_scale, 16) ||
+        !aligned(weights, 16) || !aligned(logits, 16) || !aligned(cu_seqlen_ks, 4) ||
+        !aligned(cu_seqlen_ke, 4))
+        return fail(MQA_ERR_INVALID_ARG, "data pointers must be 16-byte aligned, int32 arrays 4-byte");
+    if (int rc = check_device())
+        return rc;
+
+    mqa::PrefillLaunch p;
+    p.q = q_fp8;
+    p.k = k_fp8;
+    p.kv_scale = kv_scale;
+    p.weights = weights;
+    p.ks = cu_seqlen_ks;
+    p.ke = cu_seqlen_ke;
+    p.logits = logits;
+    p.M = M;
+    p.N = N;
+    p.clean = clean_logits ? 1 : 0;
+    // Heuristic: 4 rows per wave share each K step; 4 waves per workgroup split
+    // the columns; enough column splits that the grid holds ~2048 workgroups
+    // while each wave still gets >= 4 steps; high-m first for long causal
+    // chunks (aiter PR 5046 page, "Technical Details": N > 2048).
+    p.block_m = t.block_m ? t.block_m : 4;
+    p.num_warps = t.num_warps ? t.num_warps : 4;
+    const int64_t nrb = ceil_div(M, p.block_m);
+    const int64_t steps = ceil_div(N, 64);
+    if (t.split_n) {
+        p.split_n = t.split_n;
+    } else {
+        int64_t want = std::max<int64_t>(1, ceil_div(2048, nrb));
+        int64_t cap = std::max<int64_t>(1, steps / (4 * p.num_warps));
+        p.split_n = (int)std::min(want, cap);
+    }
+    p.reverse = t.reverse_rows ? (t.reverse_rows > 0) : (N > 2048);
+    if (nrb * p.split_n > INT32_MAX)
+        return fail(MQA_ERR_INVALID_ARG, "grid too large (row blocks %lld x split %d)", (long long)nrb,
+                    p.split_n);
+    if (trace_on())
+        std::fprintf(stderr, "[mqa] prefill M=%d N=%d block_m=%d split_n=%d warps=%d reverse=%d\n", M,
+                     N, p.block_m, p.split_n, p.num_warps, p.reverse);
+    hipError_t e = mqa::launch_prefill(p, stream);
+    if (e != hipSuccess)
+        return fail(MQA_ERR_LAUNCH, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache,
+                                       const float *weights, const int32_t *context_lens,
+                                       const int32_t *block_tables, float *logits, int batch,
+                                       int next_n, int num_heads, int head_dim, int kv_block_size,
+                                       int num_blocks, int max_blocks_per_seq, int max_model_len,
+                                       int clean_logits, const mqa_tunables *tun,
+                                       hipStream_t stream)
+{
+    if (batch < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_model_len < 0)
+        return fail(MQA_ERR_INVALID_ARG, "negative size argument");
+    if (next_n < 1 || next_n > 8)
+        return fail(MQA_ERR_INVALID_ARG, "next_n must be in 1..8 (got %d)", next_n);
+    if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
+        return fail(MQA_ERR_UNSUPPORTED,
+                    "decode supports num_heads=32, head_dim=128, kv_block_size=64 (got %d, %d, %d)",
+                    num_heads, head_dim, kv_block_size);
+    mqa_tunables t = {};
+    if (tun)
+        t = *tun;
+    if (t.rows_per_block < 0 || t.rows_per_block > 8 || t.split_kv < 0 || t.num_warps < 0 ||
+        t.num_warps > 4)
+        return fail(MQA_ERR_INVALID_ARG, "rows_per_block in 0..8, split_kv >= 0, num_warps in 0..4");
+    if (batch == 0 || max_model_len == 0)
+        return ok();
+    if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables || !logits)
+        return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(q_fp8, 16) || !aligned(kv_cache, 16) || !aligned(weights, 16) ||
+        !aligned(logits, 16) || !aligned(context_lens, 4) || !aligned(block_tables, 4))
+        return fail(MQA_ERR_INVALID_ARG, "data pointers must be 16-byte aligned, int32 arrays 4-byte");
+    if (int rc = check_device())
+        return rc;
+
+    mqa::DecodeLaunch p;
+    p.q = q_fp8;
+    p.cache = kv_cache;
+    p.weights = weights;
+    p.context_lens = context_lens;
+    p.block_tables = block_tables;
+    p.logits = logits;
+    p.batch = batch;
+    p.next_n = next_n;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_model_len = max_model_len;
+    p.clean = clean_logits ? 1 : 0;
+    // Heuristic (aiter PR 5047 page, "Technical Details": rows per K stream and
+    // the KV split are chosen on the host from batch * max_model_len, since the
+    // device-resident context lengths are not visible without a sync).
+    //   rows: all next_n rows share one K stream up to 4; above that two row
+    //         groups (e.g. 6 -> 2 x 3) keep Q + weights within the register
+    //         budget, and the second group's K reads hit L2.
+    //   split: aim at ~8 waves per SIMD worth of work items so ragged
+    //         sequences balance, with >= 2 steps per wave.
+    int rows = t.rows_per_block ? t.rows_per_block : (next_n <= 4 ? next_n : (next_n + 1) / 2);
+    rows = std::min(rows, next_n);
+    p.rows = rows;
+    p.num_warps = t.num_warps ? t.num_warps : 4;
+    const int64_t groups = ceil_div(next_n, rows);
+    const int64_t steps_max = ceil_div(max_model_len, 64);
+    if (t.split_kv) {
+        p.split_kv = t.split_kv;
+    } else {
+        const int64_t total = (int64_t)batch * groups * steps_max;
+        const int64_t per_wave = std::max<int64_t>(2, total / 8192);
+        p.split_kv = (int)std::max<int64_t>(1, ceil_div(steps_max, per_wave * p.num_warps));
+    }
+    if ((int64_t)batch * groups * p.split_kv > INT32_MAX)
+        return fail(MQA_ERR_INVALID_ARG, "grid too large");
+    if (trace_on())
+        std::fprintf(stderr, "[mqa] decode B=%d next_n=%d mml=%d rows=%d split_kv=%d warps=%d\n", batch,
+                     next_n, max_model_len, p.rows, p.split_kv, p.num_warps);
+    hipError_t e = mqa::launch_decode(p, stream);
+    if (e != hipSuccess)
+        return fail(MQA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}

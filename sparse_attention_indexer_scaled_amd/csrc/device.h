@@ -1,0 +1,155 @@
+// Device building blocks shared by the prefill and decode kernels (gfx950).
+//
+// One wave (64 lanes) computes the scores of one query row against a 32-token
+// K tile with two fp8 MFMAs, v_mfma_f32_32x32x64_f8f6f4: A = the row's Q
+// (32 heads x 128 dims), B = K^T (128 dims x 32 tokens), D = S[head][token] in
+// fp32.  The contraction is a dense 32-head x token matrix product, which is
+// why it runs on the matrix cores (both pages, "Technical Details": 32 heads x
+// 32 tokens per fp8 MFMA tile).
+//
+// Operand placement.  Lane l = 32 g + t (t = l & 31, g = l >> 5) holds, for row
+// t of its operand (a head of Q, a token of K), the four 16-byte chunks at
+// bytes (2j + g) * 16, j = 0..3.  Chunks j = 0, 1 feed the first MFMA (dims
+// 0..63), chunks 2, 3 the second (dims 64..127).  The MFMA pairs A's byte slot
+// (lane group, byte) with B's identical slot, so any placement that Q and K
+// share computes the full dot product; this one lets lanes t and t + 32 read
+// 32 adjacent bytes of the same K row per load instruction.
+//
+// Result placement (32x32 fp32 accumulator): lane l holds token t = l & 31 and
+// the 16 heads 8 (r / 4) + 4 g + (r % 4), r = 0..15.  The ReLU . weight
+// epilogue therefore runs in-lane over 16 heads, and the head sum needs only
+// one cross-lane step between lane t and lane t + 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+constexpr int kHeads = 32;
+constexpr int kDim = 128;
+constexpr int kTile = 32;  // tokens per MFMA column tile
+constexpr int kStep = 64;  // tokens per wave step: two tiles
+constexpr int kBlock = 64; // paged-cache block size supported by the decode kernel
+constexpr int kBlockBytes = kBlock * (kDim + 4);
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 64 fp8 bytes per lane of one 32-row x 128-dim operand (a K tile or a Q row).
+struct Frag {
+    i32x4 c[4];
+};
+
+// The 16 head weights matching this lane's accumulator registers.
+struct Weights16 {
+    f32x4 c[4];
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Row `rowptr` is this lane's own row (head or token) of the operand.
+__device__ __forceinline__ void load_frag(Frag &f, const uint8_t *rowptr, int lane)
+{
+    const uint8_t *p = rowptr + (lane >> 5) * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        f.c[j] = *reinterpret_cast<const i32x4 *>(p + 32 * j);
+}
+
+__device__ __forceinline__ void load_frag_nt(Frag &f, const uint8_t *rowptr, int lane)
+{
+    const uint8_t *p = rowptr + (lane >> 5) * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        f.c[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p + 32 * j));
+}
+
+// wrow: the 32 fp32 weights of one query row.  Register r of the accumulator
+// holds head 8 (r / 4) + 4 g + r % 4, so chunk q covers heads 8 q + 4 g + 0..3.
+__device__ __forceinline__ void load_weights(Weights16 &w, const float *wrow, int lane)
+{
+    const float *p = wrow + (lane >> 5) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        w.c[q] = *reinterpret_cast<const f32x4 *>(p + 8 * q);
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1, f32x16 c)
+{
+    i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    i32x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    // format codes 0, 0: both operands fp8 e4m3 (OCP); zero scale operands
+    // select the unscaled instruction.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// S[head][token] for one query row and one 32-token tile.
+__device__ __forceinline__ f32x16 row_scores(const Frag &q, const Frag &k)
+{
+    f32x16 acc = {};
+    acc = mfma_fp8(q.c[0], q.c[1], k.c[0], k.c[1], acc);
+    acc = mfma_fp8(q.c[2], q.c[3], k.c[2], k.c[3], acc);
+    return acc;
+}
+
+// sum over this lane's 16 heads of relu(S) * w.  Built with -fno-honor-nans, so
+// each relu is a single v_max_f32 (no IEEE canonicalize first).
+__device__ __forceinline__ float relu_weight_sum(const f32x16 &s, const Weights16 &w)
+{
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a = fmaf(fmaxf(s[4 * q + 0], 0.f), w.c[q][0], a);
+        b = fmaf(fmaxf(s[4 * q + 1], 0.f), w.c[q][1], b);
+        a = fmaf(fmaxf(s[4 * q + 2], 0.f), w.c[q][2], a);
+        b = fmaf(fmaxf(s[4 * q + 3], 0.f), w.c[q][3], b);
+    }
+    return a + b;
+}
+
+// Finish the head sum of two rows at once.  v_permlane32_swap exchanges the
+// upper half of `a` with the lower half of `b`, so after one swap and one add
+// lanes 0..31 hold row a's 32 token sums and lanes 32..63 row b's (both pages,
+// "Technical Details": the paired-row permlane32 swap replaces a ds_bpermute
+// round trip through LDS).
+__device__ __forceinline__ float pair_head_sum(float a, float b)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Write -inf over row[c0, c1), split into `nparts` contiguous parts of which
+// this wave writes part `part`.  16-byte stores where alignment allows.
+__device__ __forceinline__ void fill_neg_inf(float *row, int64_t c0, int64_t c1, int part,
+                                             int nparts, int lane)
+{
+    if (c1 <= c0)
+        return;
+    const int64_t len = c1 - c0;
+    const int64_t a = c0 + len * part / nparts;
+    const int64_t e = c0 + len * (part + 1) / nparts;
+    if (e <= a)
+        return;
+    const float ninf = -__builtin_inff();
+    float *p = row + a;
+    int64_t n = e - a;
+    int64_t head = (int64_t)(((16u - ((uintptr_t)p & 15u)) & 15u) >> 2);
+    if (head > n)
+        head = n;
+    if (lane < head)
+        p[lane] = ninf;
+    p += head;
+    n -= head;
+    const int64_t n4 = n >> 2;
+    const f32x4 v = {ninf, ninf, ninf, ninf};
+    for (int64_t i = lane; i < n4; i += 64)
+        reinterpret_cast<f32x4 *>(p)[i] = v;
+    const int64_t tail = n & 3;
+    if (lane < tail)
+        p[n4 * 4 + lane] = ninf;
+}
+
+} // namespace mqa

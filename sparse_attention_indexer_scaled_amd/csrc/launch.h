@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI entry points (api.cpp) and the kernel
+// translation units.  Everything here is already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+struct PrefillLaunch {
+    const uint8_t *q;
+    const uint8_t *k;
+    const float *kv_scale;
+    const float *weights;
+    const int32_t *ks;
+    const int32_t *ke;
+    float *logits;
+    int M;
+    int N;
+    int clean;
+    int block_m;   // rows per wave: 1, 2, 4 or 8
+    int split_n;   // workgroups per row block
+    int num_warps; // waves per workgroup
+    int reverse;   // 1: high-m row blocks first
+};
+
+struct DecodeLaunch {
+    const uint8_t *q;
+    const uint8_t *cache;
+    const float *weights;
+    const int32_t *context_lens;
+    const int32_t *block_tables;
+    float *logits;
+    int batch;
+    int next_n;
+    int max_blocks_per_seq;
+    int64_t max_model_len;
+    int clean;
+    int rows;      // rows per wave (R), 1..8, <= next_n
+    int split_kv;  // workgroups per (sequence, row group)
+    int num_warps; // waves per workgroup
+};
+
+hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
+
+} // namespace mqa

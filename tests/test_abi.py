@@ -1,0 +1,132 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments before touching the device.
+
+Every call here fails validation before any HIP call that could launch work,
+so these tests are safe on any machine, GPU or not.  No call passes a pointer
+that would pass validation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_scaled_amd as mqa
+from sparse_attention_indexer_scaled_amd import _native
+from tests.util import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mqa_indexer.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        from sparse_attention_indexer_scaled_amd import build
+        build.build()
+    return _native.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(_native.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    # and the exports are plain C symbols (no C++ mangling)
+    out = os.popen("nm -D --defined-only %s" % _native.LIB_PATH).read()
+    for name in _declared_functions():
+        assert re.search(r"\bT %s$" % name, out, flags=re.M), name
+
+
+def test_tunables_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct mqa_tunables \{(.*?)\} mqa_tunables;", text, flags=re.S).group(1)
+    fields = re.findall(r"int\s+(\w+);", body)
+    assert fields == [f for f, _ in _native.Tunables._fields_]
+    assert ctypes.sizeof(_native.Tunables) == 4 * len(fields)
+
+
+def test_error_codes_match_header():
+    text = open(HEADER).read()
+    for name in ("MQA_OK", "MQA_ERR_INVALID_ARG", "MQA_ERR_UNSUPPORTED", "MQA_ERR_LAUNCH",
+                 "MQA_ERR_DEVICE"):
+        m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
+        assert int(m.group(1)) == getattr(_native, name), name
+
+
+def test_gate_rejects_other_shapes(lib):
+    for h, d, bs in [(64, 128, 0), (32, 64, 0), (128, 128, 64), (32, 128, 16), (32, 128, 1)]:
+        assert lib.mqa_is_supported(h, d, bs) == 0
+
+
+P = ctypes.c_void_p
+
+
+def _prefill(lib, ptrs, M=4, N=8, H=32, D=128, clean=1, tun=None):
+    return lib.mqa_logits_prefill(*ptrs, M, N, H, D, clean, tun, None)
+
+
+def _decode(lib, ptrs, B=2, nn=1, H=32, D=128, bs=64, nb=4, mbps=2, mml=128, tun=None):
+    return lib.paged_mqa_logits_decode(*ptrs, B, nn, H, D, bs, nb, mbps, mml, 1, tun, None)
+
+
+def test_prefill_validation(lib):
+    nulls = [None] * 7
+    assert _prefill(lib, nulls, M=-1) == mqa._native.MQA_ERR_INVALID_ARG
+    assert _prefill(lib, nulls, N=-5) == mqa._native.MQA_ERR_INVALID_ARG
+    assert _prefill(lib, nulls, H=64) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _prefill(lib, nulls, D=64) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert "num_heads" in mqa.last_error()
+    # empty problem: successful no-op, nothing dereferenced
+    assert _prefill(lib, nulls, M=0) == 0
+    assert _prefill(lib, nulls, N=0) == 0
+    assert mqa.last_error() == ""
+    assert _prefill(lib, nulls) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "NULL" in mqa.last_error()
+    # misaligned (never dereferenced: rejected before the device is touched)
+    odd = [P(0x1001)] * 7
+    assert _prefill(lib, odd) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "aligned" in mqa.last_error()
+    bad = _native.Tunables(block_m=3)
+    assert _prefill(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    bad = _native.Tunables(reverse_rows=2)
+    assert _prefill(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    bad = _native.Tunables(num_warps=9)
+    assert _prefill(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+
+
+def test_decode_validation(lib):
+    nulls = [None] * 6
+    assert _decode(lib, nulls, B=-1) == mqa._native.MQA_ERR_INVALID_ARG
+    assert _decode(lib, nulls, nn=0) == mqa._native.MQA_ERR_INVALID_ARG
+    assert _decode(lib, nulls, nn=9) == mqa._native.MQA_ERR_INVALID_ARG
+    assert _decode(lib, nulls, bs=16) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, bs=0) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, H=64) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, B=0) == 0
+    assert _decode(lib, nulls, mml=0) == 0
+    assert _decode(lib, nulls) == mqa._native.MQA_ERR_INVALID_ARG
+    odd = [P(0x2002)] * 6
+    assert _decode(lib, odd) == mqa._native.MQA_ERR_INVALID_ARG
+    bad = _native.Tunables(rows_per_block=9)
+    assert _decode(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+
+
+def test_binding_raises_on_missing_library(tmp_path):
+    saved = _native._lib
+    _native._lib = None
+    try:
+        with pytest.raises(mqa.MQAError):
+            _native.load_library(str(tmp_path / "nope.so"))
+    finally:
+        _native._lib = saved

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded bytes.  Small and mid sizes are compared element by element in
+full; they span several 64-token steps, ragged tails, every window mode, both
+clean_logits settings, every next_n in 1..8 and every rows-per-wave
+instantiation.  The full-size workloads are in test_gpu_workloads.py.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_indexer_scaled_amd import Tunables, inputs
+from tests.gpu_util import (assert_parity, lib, oracle_decode, oracle_prefill, run_decode,
+                            run_prefill, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    lib()
+    from sparse_attention_indexer_scaled_amd import is_supported
+    assert is_supported(32, 128, 0) and is_supported(32, 128, 64)
+
+
+# ---------------------------------------------------------------------------
+# exact integer pin: every intermediate is an exact fp32 value, so the GPU
+# must equal the oracle bit for bit whatever its accumulation order.  This pins
+# the fp8 format, the operand byte placement, the head <-> weight pairing and
+# the lane layout of the cross-head reduction.
+# ---------------------------------------------------------------------------
+
+
+def _int_prefill(M, N, seed):
+    rng = np.random.default_rng(seed)
+    p = inputs.make_prefill(M, N, seed)
+    p.q = inputs.to_fp8_bytes(rng.integers(-16, 17, (M, 32, 128)).astype(np.float32))
+    p.k = inputs.to_fp8_bytes(rng.integers(-16, 17, (N, 128)).astype(np.float32))
+    p.weights = (rng.choice([-1, 1], (M, 32)) * 2.0 ** -rng.integers(0, 4, (M, 32))).astype(np.float32)
+    p.kv_scale = rng.choice([0.5, 1.0, 2.0], N).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("block_m", [1, 2, 4, 8])
+def test_prefill_integer_inputs_bit_exact(block_m):
+    p = _int_prefill(21, 333, seed=block_m)
+    say("prefill int M=21 N=333 block_m=%d" % block_m)
+    out = run_prefill(p, tun=Tunables(block_m=block_m))
+    ref, _ = oracle_prefill(p)
+    if not np.array_equal(out, ref):
+        bad = np.argwhere(out != ref)
+        say("first mismatches (m, n, gpu, ref): %s" % [(int(m), int(n), float(out[m, n]), float(ref[m, n])) for m, n in bad[:8]])
+    assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("next_n", [1, 2, 3, 5, 8])
+def test_decode_integer_inputs_bit_exact(next_n):
+    rng = np.random.default_rng(next_n)
+    d = inputs.make_decode(3, next_n, [700, 64, 131], 800, seed=next_n, poison=True)
+    d.q = inputs.to_fp8_bytes(rng.integers(-16, 17, d.q.shape).astype(np.float32))
+    d.weights = (rng.choice([-1, 1], d.weights.shape) * 2.0 ** -rng.integers(0, 4, d.weights.shape)).astype(np.float32)
+    kview, sview = inputs.cache_views(d.kv_cache, 64, 128)
+    used = d.num_blocks - 1  # the last block is the poison block
+    kview[:used] = inputs.to_fp8_bytes(rng.integers(-16, 17, kview[:used].shape).astype(np.float32))
+    sview[:used] = rng.choice([0.5, 1.0, 2.0], sview[:used].shape).astype(np.float32)
+    say("decode int next_n=%d" % next_n)
+    out = run_decode(d)
+    ref, _, _ = oracle_decode(d)
+    assert np.array_equal(out, ref)
+
+
+# ---------------------------------------------------------------------------
+# random inputs (the workloads' distributions), element by element
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # (M, N, window mode)
+    (64, 512, "causal"),
+    (37, 517, "causal"),
+    (70, 700, "cp"),
+    (33, 300, "misaligned"),
+    (40, 260, "empty"),
+    (29, 200, "past_end"),
+    (64, 640, "multi_req"),
+    (5, 3, "causal"),
+    (1, 1, "causal"),
+    (3, 2000, "causal"),
+]
+
+
+@pytest.mark.parametrize("M,N,mode", PREFILL_CASES, ids=[f"{m}x{n}-{w}" for m, n, w in PREFILL_CASES])
+@pytest.mark.parametrize("clean", [1, 0])
+def test_prefill_matches_oracle(M, N, mode, clean):
+    p = inputs.make_prefill(M, N, seed=100 + M + N, windows=mode)
+    say("prefill M=%d N=%d mode=%s clean=%d" % (M, N, mode, clean))
+    out = run_prefill(p, clean=bool(clean))
+    ref, mag = oracle_prefill(p)
+    if clean:
+        assert_parity(out, ref, mag, f"prefill_{M}x{N}_{mode}")
+    else:
+        win = np.isfinite(ref)
+        assert np.isnan(out[~win]).all(), "clean_logits=0 wrote outside the window"
+        out_w = np.where(win, out, -np.inf)
+        assert_parity(out_w, ref, mag, f"prefill_{M}x{N}_{mode}_noclean")
+
+
+DECODE_CASES = [
+    # (B, next_n, context lens, max_model_len)
+    (2, 1, [1000, 333], 1024),
+    (3, 2, [64, 65, 63], 200),
+    (2, 3, [1, 2], 130),          # contexts shorter than next_n
+    (4, 4, [0, 3, 700, 4096], 4096),
+    (2, 5, [513, 1111], 1200),
+    (2, 6, [2000, 7], 2001),      # max_model_len not a multiple of 64
+    (1, 7, [300], 333),
+    (2, 8, [129, 1025], 1100),
+]
+
+
+@pytest.mark.parametrize("B,next_n,ctx,mml", DECODE_CASES,
+                         ids=[f"B{b}-nn{n}-mml{m}" for b, n, _, m in DECODE_CASES])
+@pytest.mark.parametrize("clean", [1, 0])
+def test_decode_matches_oracle(B, next_n, ctx, mml, clean):
+    d = inputs.make_decode(B, next_n, ctx, mml, seed=200 + next_n, poison=True)
+    say("decode B=%d next_n=%d ctx=%s mml=%d clean=%d" % (B, next_n, ctx, mml, clean))
+    out = run_decode(d, clean=bool(clean))
+    ref, mag, _ = oracle_decode(d)
+    if clean:
+        assert_parity(out, ref, mag, f"decode_B{B}_nn{next_n}")
+    else:
+        win = np.isfinite(ref)
+        assert np.isnan(out[~win]).all(), "clean_logits=0 wrote outside the window"
+        assert_parity(np.where(win, out, -np.inf), ref, mag, f"decode_B{B}_nn{next_n}_noclean")
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_decode_every_row_grouping(rows):
+    """Every rows-per-wave instantiation, including groups that do not divide
+    next_n (the last group is short)."""
+    d = inputs.make_decode(2, 8, [900, 77], 1000, seed=300 + rows, poison=True)
+    say("decode rows_per_block=%d" % rows)
+    out = run_decode(d, tun=Tunables(rows_per_block=rows))
+    ref, mag, _ = oracle_decode(d)
+    assert_parity(out, ref, mag, f"decode_rows{rows}")
+
+
+# ---------------------------------------------------------------------------
+# GPU self-invariants (bitwise)
+# ---------------------------------------------------------------------------
+
+
+def test_prefill_tunables_do_not_change_bits():
+    p = inputs.make_prefill(45, 1500, seed=401, windows="multi_req")
+    base = run_prefill(p)
+    for tun in [Tunables(block_m=1), Tunables(block_m=2, split_n=3), Tunables(block_m=8, num_warps=1),
+                Tunables(split_n=7, num_warps=2, reverse_rows=1), Tunables(reverse_rows=-1),
+                Tunables(block_m=4, split_n=40, num_warps=3)]:
+        say("prefill tunables %s" % [getattr(tun, f) for f, _ in Tunables._fields_])
+        assert np.array_equal(run_prefill(p, tun=tun), base, equal_nan=True)
+
+
+def test_decode_tunables_do_not_change_bits():
+    d = inputs.make_decode(3, 6, [2000, 150, 1300], 2048, seed=402, poison=True)
+    base = run_decode(d)
+    for tun in [Tunables(rows_per_block=1), Tunables(rows_per_block=6, split_kv=1),
+                Tunables(rows_per_block=3, split_kv=9, num_warps=1), Tunables(split_kv=64),
+                Tunables(rows_per_block=4, num_warps=2), Tunables(rows_per_block=2, split_kv=5, num_warps=3)]:
+        say("decode tunables %s" % [getattr(tun, f) for f, _ in Tunables._fields_])
+        assert np.array_equal(run_decode(d, tun=tun), base, equal_nan=True)
+
+
+def test_decode_block_pool_permutation_invariance():
+    """Moving the physical blocks around (and updating the table) must not
+    change a single bit: the kernel reads K through the table, not by walking
+    the cache."""
+    d = inputs.make_decode(3, 2, [500, 64, 1000], 1024, seed=403)
+    base = run_decode(d)
+    perm = np.random.default_rng(0).permutation(d.num_blocks)
+    inv = np.argsort(perm)
+    d.kv_cache = d.kv_cache[perm]          # new block i holds old block perm[i]
+    d.block_tables = inv[d.block_tables].astype(np.int32)
+    assert np.array_equal(run_decode(d), base)
+
+
+def test_power_of_two_homogeneity():
+    """Doubling kv_scale or the weights doubles every finite output exactly."""
+    p = inputs.make_prefill(17, 400, seed=404)
+    base = run_prefill(p)
+    p2 = inputs.make_prefill(17, 400, seed=404)
+    p2.kv_scale = p2.kv_scale * np.float32(2)
+    assert np.array_equal(run_prefill(p2), np.where(np.isfinite(base), 2 * base, base))
+    p3 = inputs.make_prefill(17, 400, seed=404)
+    p3.weights = p3.weights * np.float32(0.5)
+    assert np.array_equal(run_prefill(p3), np.where(np.isfinite(base), 0.5 * base, base))
+
+
+def test_paged_decode_equals_contiguous_prefill_on_gpu():
+    """Row (b, j) of decode equals the prefill kernel over that sequence's K with
+    ks = 0, ke = ctx - next_n + j + 1 (within the fp32 bound; the two kernels
+    may order their sums differently)."""
+    d = inputs.make_decode(2, 3, [777, 130], 800, seed=405, poison=True)
+    dec = run_decode(d)
+    for b in range(2):
+        ctx = int(d.context_lens[b])
+        p = inputs.PrefillInputs(d.q[b], d.k_seq[b], d.s_seq[b], d.weights[b * 3:(b + 1) * 3],
+                                 np.zeros(3, np.int32), (ctx - 3 + np.arange(3) + 1).astype(np.int32))
+        pre = run_prefill(p)
+        ref = np.full((3, 800), -np.inf)
+        ref[:, :ctx] = pre
+        _, mag_full, _ = oracle_decode(d, seqs=[b])
+        assert_parity(dec[b * 3:(b + 1) * 3], ref, mag_full, f"paged_vs_contig_{b}")
+
+
+def test_empty_problems_are_noops():
+    from sparse_attention_indexer_scaled_amd import mqa_logits_prefill, paged_mqa_logits_decode
+    z8 = torch.zeros((0, 32, 128), dtype=torch.uint8, device="cuda")
+    k = torch.zeros((5, 128), dtype=torch.uint8, device="cuda")
+    out = mqa_logits_prefill(z8, k, torch.ones(5, device="cuda"), torch.zeros((0, 32), device="cuda"),
+                             torch.zeros(0, dtype=torch.int32, device="cuda"),
+                             torch.zeros(0, dtype=torch.int32, device="cuda"))
+    assert out.shape == (0, 5)
+    q = torch.zeros((0, 1, 32, 128), dtype=torch.uint8, device="cuda")
+    cache = torch.zeros((1, 64 * 132), dtype=torch.uint8, device="cuda")
+    out = paged_mqa_logits_decode(q, cache, torch.zeros((0, 32), device="cuda"),
+                                  torch.zeros(0, dtype=torch.int32, device="cuda"),
+                                  torch.zeros((0, 1), dtype=torch.int32, device="cuda"), 64)
+    assert out.shape == (0, 64)
+    torch.cuda.synchronize()
