@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--hot", action="store_true", help="one input copy (MALL-warm)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--tunables", default="",
+                    help="launch overrides, e.g. rows_per_block=3,split_kv=64 (0 = heuristic)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -66,7 +68,7 @@ def cpu_model():
 class Workload:
     """Device-resident input copies and output buffers for one named workload."""
 
-    def __init__(self, idx, hot):
+    def __init__(self, idx, hot, tunables=None):
         import torch
         from sparse_attention_indexer_scaled_amd import inputs, workload
         self.idx = idx
@@ -100,23 +102,34 @@ class Workload:
         self.outs = [torch.empty(self.out_shape, dtype=torch.float32, device="cuda")
                      for _ in range(nsets)]
         self.nsets = nsets
+        self.tun = tunables
 
     def call(self, i):
         from sparse_attention_indexer_scaled_amd import mqa_logits_prefill, paged_mqa_logits_decode
         s = self.sets[i % self.nsets]
         out = self.outs[i % self.nsets]
         if self.kind == "prefill":
-            mqa_logits_prefill(s["q"], s["k"], s["sc"], s["w"], s["ks"], s["ke"], logits=out)
+            mqa_logits_prefill(s["q"], s["k"], s["sc"], s["w"], s["ks"], s["ke"], logits=out,
+                               tunables=self.tun)
         else:
             paged_mqa_logits_decode(s["q"], s["cache"], s["w"], s["ctx"], s["bt"],
-                                    self.host.max_model_len, logits=out)
+                                    self.host.max_model_len, logits=out, tunables=self.tun)
 
 
-def time_workload(wl, steps, warmup, graph=True):
+def time_workload(wl, steps, warmup, graph=True, settle_s=0.3):
+    """Per-call milliseconds of exactly `steps` calls.  Warm-up: `warmup`
+    calls, extended until about settle_s of GPU work has run so that clocks
+    have left their idle state before the timed region."""
     import torch
-    for i in range(warmup):
+    t0 = time.time()
+    i = 0
+    while i < warmup or time.time() - t0 < settle_s:
         wl.call(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    wl.warmup_done = i
     stream = torch.cuda.current_stream()
     if graph:
         g = torch.cuda.CUDAGraph()
@@ -181,6 +194,17 @@ def cpu_baseline(wl, budget_s=12.0):
                       % (len(done), h.B, h.next_n, wl.cfg["name"])}
 
 
+def parse_tunables(text):
+    if not text:
+        return None
+    from sparse_attention_indexer_scaled_amd import Tunables
+    t = Tunables()
+    for item in text.split(","):
+        k, v = item.split("=")
+        setattr(t, k.strip(), int(v))
+    return t
+
+
 def calib_copy(mib):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -211,11 +235,12 @@ def main():
         calib_copy(args.calib_copy)
         return
 
+    tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
         [i for i in (1, 4, 3, 0) if i != args.workload]
     results, head = {}, None
     for idx in order:
-        wl = Workload(idx, args.hot)
+        wl = Workload(idx, args.hot, tun)
         ms = time_workload(wl, args.steps, args.warmup, graph=not args.no_graph)
         results[wl.cfg["name"]] = summarize(wl, ms)
         print("[bench] %s: %.2f us/call" % (wl.cfg["name"], ms * 1e3), file=sys.stderr, flush=True)
@@ -235,7 +260,7 @@ def main():
         "unit": "TB/s" if decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": wl.warmup_done,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",

@@ -55,13 +55,15 @@ extern "C" {
  *   prefill:
  *     block_m      query rows that share one K stream per wave: 1, 2, 4 or 8
  *     split_n      workgroups per row block along the columns, >= 1
- *     num_warps    waves per workgroup (they split the column range), 1..8
+ *     num_warps    waves per workgroup (they split the column range), 1..4
  *     reverse_rows 1 = dispatch row blocks high-m first, -1 = natural order
  *   decode:
  *     rows_per_block  next_n rows that share one K stream per wave, 1..8
- *                     (clamped to next_n)
- *     split_kv        workgroups per (sequence, row group) along KV, >= 1
- *     num_warps       as above
+ *                     (clamped to next_n); ceil(next_n / rows_per_block)
+ *                     row-group waves walk each K stream side by side
+ *     split_kv        workgroups per sequence along KV, >= 1
+ *     num_warps       K streams per workgroup; num_warps x row groups must
+ *                     not exceed 8 waves (4 when rows_per_block > 4)
  */
 typedef struct mqa_tunables {
     int block_m;

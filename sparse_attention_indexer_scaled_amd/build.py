@@ -28,7 +28,7 @@ SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
-DEVICE = ["--offload-arch=gfx950", "-fno-honor-nans",
+DEVICE = ["--offload-arch=gfx950", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -196,8 +196,8 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     if (tun)
         t = *tun;
     if (t.rows_per_block < 0 || t.rows_per_block > 8 || t.split_kv < 0 || t.num_warps < 0 ||
-        t.num_warps > 4)
-        return fail(MQA_ERR_INVALID_ARG, "rows_per_block in 0..8, split_kv >= 0, num_warps in 0..4");
+        t.num_warps > 8)
+        return fail(MQA_ERR_INVALID_ARG, "rows_per_block in 0..8, split_kv >= 0, num_warps in 0..8");
     if (batch == 0 || max_model_len == 0)
         return ok();
     if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables || !logits)
@@ -223,25 +223,33 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     // Heuristic (aiter PR 5047 page, "Technical Details": rows per K stream and
     // the KV split are chosen on the host from batch * max_model_len, since the
     // device-resident context lengths are not visible without a sync).
-    //   rows: all next_n rows share one K stream up to 4; above that two row
-    //         groups (e.g. 6 -> 2 x 3) keep Q + weights within the register
-    //         budget, and the second group's K reads hit L2.
-    //   split: aim at ~8 waves per SIMD worth of work items so ragged
-    //         sequences balance, with >= 2 steps per wave.
+    //   rows: all next_n rows share one wave's K stream up to 4 (Q + weights
+    //         = 32 VGPR per row); above that two row groups (e.g. 6 -> 2 x 3)
+    //         whose waves walk the same blocks side by side (L1 hits).
+    //   waves: 4 waves per workgroup (measured better than 8); a workgroup
+    //         may hold up to 8 while a wave fits 256 registers, 4 beyond.
+    //   split: ~2 workgroups per CU in total, but at least 2 steps per wave.
     int rows = t.rows_per_block ? t.rows_per_block : (next_n <= 4 ? next_n : (next_n + 1) / 2);
     rows = std::min(rows, next_n);
     p.rows = rows;
-    p.num_warps = t.num_warps ? t.num_warps : 4;
-    const int64_t groups = ceil_div(next_n, rows);
+    const int groups = (next_n + rows - 1) / rows;
+    const int max_waves = rows <= 4 ? 8 : 4;
+    if (groups > max_waves)
+        return fail(MQA_ERR_INVALID_ARG, "rows_per_block=%d gives %d row groups; at most %d fit a workgroup",
+                    rows, groups, max_waves);
+    p.num_warps = t.num_warps ? t.num_warps : std::max(1, 4 / groups);
+    if (p.num_warps * groups > max_waves)
+        return fail(MQA_ERR_INVALID_ARG, "num_warps=%d x %d row groups exceeds %d waves per workgroup",
+                    p.num_warps, groups, max_waves);
     const int64_t steps_max = ceil_div(max_model_len, 64);
     if (t.split_kv) {
         p.split_kv = t.split_kv;
     } else {
-        const int64_t total = (int64_t)batch * groups * steps_max;
-        const int64_t per_wave = std::max<int64_t>(2, total / 8192);
-        p.split_kv = (int)std::max<int64_t>(1, ceil_div(steps_max, per_wave * p.num_warps));
+        const int64_t want = ceil_div(512, batch);
+        const int64_t cap = std::max<int64_t>(1, steps_max / (2 * p.num_warps));
+        p.split_kv = (int)std::max<int64_t>(1, std::min(want, cap));
     }
-    if ((int64_t)batch * groups * p.split_kv > INT32_MAX)
+    if ((int64_t)batch * p.split_kv > INT32_MAX)
         return fail(MQA_ERR_INVALID_ARG, "grid too large");
     if (trace_on())
         std::fprintf(stderr, "[mqa] decode B=%d next_n=%d mml=%d rows=%d split_kv=%d warps=%d\n", batch,

@@ -28,14 +28,9 @@
 namespace mqa {
 namespace {
 
+// Sizes and launch shape; the pointers are separate __restrict__ kernel
+// arguments so the compiler knows the output never aliases an input.
 struct PrefillArgs {
-    const uint8_t *q;
-    const uint8_t *k;
-    const float *sc;
-    const float *w;
-    const int32_t *ks;
-    const int32_t *ke;
-    float *out;
     int M;
     int N;
     int clean;
@@ -63,9 +58,38 @@ __device__ __forceinline__ void load_kstep(KStep &k, const uint8_t *kbuf, const 
     k.sc[1] = scale[n_b];
 }
 
+// Scores, relu.weight sums and kv-scaled head sums for one 64-column step and
+// the wave's BM rows; tot[h][i] is row pair i of tile h (lanes 0..31 row 2i,
+// lanes 32..63 row 2i + 1).  Branch-free so one row's epilogue (VALU) can
+// overlap the next row's MFMAs.
 template <int BM>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
+__device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[BM],
+                                            const Weights16 (&w)[BM], float (&tot)[2][(BM + 1) / 2])
 {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float part[BM];
+#pragma unroll
+        for (int r = 0; r < BM; ++r)
+            part[r] = relu_weight_sum(row_scores(q[r], k.t[h]), w[r]);
+#pragma unroll
+        for (int i = 0; i < (BM + 1) / 2; ++i) {
+            const float pb = (2 * i + 1 < BM) ? part[(2 * i + 1 < BM) ? 2 * i + 1 : 2 * i] : part[2 * i];
+            tot[h][i] = pair_head_sum(part[2 * i], pb) * k.sc[h];
+        }
+    }
+}
+
+template <int BM>
+__global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict__ qbuf,
+                                                      const uint8_t *__restrict__ kbuf,
+                                                      const float *__restrict__ scale,
+                                                      const float *__restrict__ wbuf,
+                                                      const int32_t *__restrict__ ks,
+                                                      const int32_t *__restrict__ ke,
+                                                      float *__restrict__ logits, PrefillArgs a)
+{
+    constexpr int NP = (BM + 1) / 2;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
@@ -86,8 +110,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
         lo[r] = 0;
         hi[r] = 0;
         if (r < nrows) {
-            lo[r] = max(a.ks[m0 + r], 0);
-            hi[r] = min(a.ke[m0 + r], N);
+            lo[r] = max(ks[m0 + r], 0);
+            hi[r] = min(ke[m0 + r], N);
             if (hi[r] > lo[r]) {
                 ulo = min(ulo, lo[r]);
                 uhi = max(uhi, hi[r]);
@@ -98,64 +122,76 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
         ulo = 0;
         uhi = 0;
     }
-    const int64_t sb = ulo / kStep;
-    const int64_t se = ((int64_t)uhi + kStep - 1) / kStep;
-    const int64_t nsteps = se - sb;
-    const int64_t st0 = sb + nsteps * s / a.split;
-    const int64_t st1 = sb + nsteps * (s + 1) / a.split;
-    float *out = a.out + (int64_t)m0 * N;
+    const int sb = ulo / kStep;
+    const int se = (uhi + kStep - 1) / kStep;
+    const int nsteps = se - sb;
+    const int st0 = sb + (int)((int64_t)nsteps * s / a.split);
+    const int st1 = sb + (int)((int64_t)nsteps * (s + 1) / a.split);
+    float *out = logits + (int64_t)m0 * N;
     const int t = lane & 31;
+    const int half = lane >> 5;
+    // Window of this lane's row in each pair.
+    int rlo[NP], rhi[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int ra = 2 * i, rb2 = (2 * i + 1 < BM) ? 2 * i + 1 : 2 * i;
+        rlo[i] = half ? lo[rb2] : lo[ra];
+        rhi[i] = half ? hi[rb2] : hi[ra];
+        if (half && 2 * i + 1 >= BM)
+            rhi[i] = 0; // no such row
+    }
 
-    int64_t st = st0 + wave;
+    int st = st0 + wave;
     if (st < st1) {
         Frag q[BM];
         Weights16 w[BM];
 #pragma unroll
         for (int r = 0; r < BM; ++r) {
-            if (r < nrows) {
-                load_frag(q[r], a.q + (int64_t)(m0 + r) * (kHeads * kDim) + t * kDim, lane);
-                load_weights(w[r], a.w + (int64_t)(m0 + r) * kHeads, lane);
-            }
+            const int64_t row = m0 + min(r, nrows - 1);
+            load_frag(q[r], qbuf + row * (kHeads * kDim) + t * kDim, lane);
+            load_weights(w[r], wbuf + row * kHeads, lane);
         }
-        KStep cur;
-        load_kstep(cur, a.k, a.sc, st * kStep, N, lane);
-        for (; st < st1; st += nw) {
-            const int64_t sn = min(st + nw, st1 - 1);
-            KStep nxt;
-            load_kstep(nxt, a.k, a.sc, sn * kStep, N, lane);
+        auto store_step = [&](int step, const float (&tot)[2][NP]) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int64_t n = st * kStep + h * kTile + t;
-                float part[BM];
+                const int n = step * kStep + h * kTile + t;
 #pragma unroll
-                for (int r = 0; r < BM; ++r)
-                    if (r < nrows)
-                        part[r] = relu_weight_sum(row_scores(q[r], cur.t[h]), w[r]);
-#pragma unroll
-                for (int r = 0; r < BM; r += 2) {
-                    if (r < nrows) {
-                        const bool has_b = (r + 1 < nrows);
-                        // has_b implies r + 1 < BM; the clamp only keeps the
-                        // index in range for the compiler.
-                        const float pb = has_b ? part[(r + 1 < BM) ? r + 1 : r] : part[r];
-                        const float tot = pair_head_sum(part[r], pb) * cur.sc[h];
-                        const int rr = (lane < 32) ? r : r + 1;
-                        const int rlo = (lane < 32) ? lo[r] : lo[(r + 1 < BM) ? r + 1 : r];
-                        const int rhi = (lane < 32) ? hi[r] : hi[(r + 1 < BM) ? r + 1 : r];
-                        const bool valid = n >= rlo && n < rhi;
-                        if ((lane < 32 || has_b) && n < N && (valid || a.clean))
-                            out[(int64_t)rr * N + n] = valid ? tot : ninf;
-                    }
+                for (int i = 0; i < NP; ++i) {
+                    const int rr = 2 * i + half;
+                    const bool valid = n >= rlo[i] && n < rhi[i];
+                    if (rr < nrows && n < N && (valid || a.clean))
+                        out[(int64_t)rr * N + n] = valid ? tot[h][i] : ninf;
                 }
             }
-            cur = nxt;
+        };
+        // Two step buffers used alternately; each half issues the next
+        // step's loads before waiting for the current one (the
+        // sched_barrier keeps the compiler from hoisting the wait above them).
+        KStep A, B;
+        load_kstep(A, kbuf, scale, (int64_t)st * kStep, N, lane);
+        while (true) {
+            load_kstep(B, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            float tot[2][NP];
+            step_scores<BM>(A, q, w, tot);
+            store_step(st, tot);
+            st += nw;
+            if (st >= st1)
+                break;
+            load_kstep(A, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            step_scores<BM>(B, q, w, tot);
+            store_step(st, tot);
+            st += nw;
+            if (st >= st1)
+                break;
         }
     }
     if (a.clean) {
         const int part = s * nw + wave;
         const int nparts = a.split * nw;
-        const int64_t left = min(sb * kStep, (int64_t)N);
-        const int64_t right = min(se * kStep, (int64_t)N);
+        const int64_t left = min((int64_t)sb * kStep, (int64_t)N);
+        const int64_t right = min((int64_t)se * kStep, (int64_t)N);
         for (int r = 0; r < nrows; ++r) {
             fill_neg_inf(out + (int64_t)r * N, 0, left, part, nparts, lane);
             fill_neg_inf(out + (int64_t)r * N, right, N, part, nparts, lane);
@@ -164,9 +200,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
 }
 
 template <int BM>
-hipError_t launch_bm(const PrefillArgs &a, int grid, int block, hipStream_t stream)
+hipError_t launch_bm(const PrefillLaunch &p, const PrefillArgs &a, int grid, int block,
+                     hipStream_t stream)
 {
-    hipLaunchKernelGGL(prefill_kernel<BM>, dim3(grid), dim3(block), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<BM>, dim3(grid), dim3(block), 0, stream, p.q, p.k,
+                       p.kv_scale, p.weights, p.ks, p.ke, p.logits, a);
     return hipGetLastError();
 }
 
@@ -175,13 +213,6 @@ hipError_t launch_bm(const PrefillArgs &a, int grid, int block, hipStream_t stre
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream)
 {
     PrefillArgs a;
-    a.q = p.q;
-    a.k = p.k;
-    a.sc = p.kv_scale;
-    a.w = p.weights;
-    a.ks = p.ks;
-    a.ke = p.ke;
-    a.out = p.logits;
     a.M = p.M;
     a.N = p.N;
     a.clean = p.clean;
@@ -191,10 +222,10 @@ hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream)
     const int grid = a.nrb * a.split;
     const int block = 64 * p.num_warps;
     switch (p.block_m) {
-    case 1: return launch_bm<1>(a, grid, block, stream);
-    case 2: return launch_bm<2>(a, grid, block, stream);
-    case 4: return launch_bm<4>(a, grid, block, stream);
-    case 8: return launch_bm<8>(a, grid, block, stream);
+    case 1: return launch_bm<1>(p, a, grid, block, stream);
+    case 2: return launch_bm<2>(p, a, grid, block, stream);
+    case 4: return launch_bm<4>(p, a, grid, block, stream);
+    case 8: return launch_bm<8>(p, a, grid, block, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -167,7 +167,7 @@ def test_decode_tunables_do_not_change_bits():
     base = run_decode(d)
     for tun in [Tunables(rows_per_block=1), Tunables(rows_per_block=6, split_kv=1),
                 Tunables(rows_per_block=3, split_kv=9, num_warps=1), Tunables(split_kv=64),
-                Tunables(rows_per_block=4, num_warps=2), Tunables(rows_per_block=2, split_kv=5, num_warps=3)]:
+                Tunables(rows_per_block=4, num_warps=2), Tunables(rows_per_block=6, num_warps=4, split_kv=3), Tunables(rows_per_block=2, split_kv=5, num_warps=2)]:
         say("decode tunables %s" % [getattr(tun, f) for f, _ in Tunables._fields_])
         assert np.array_equal(run_decode(d, tun=tun), base, equal_nan=True)
 
