@@ -12,9 +12,10 @@ relu.weight epilogue, lane-permute head reduce, kv-scale, masked store and
 on); the other four named workloads are measured in the same run and reported
 under "workloads".
 
-Timing: W eager warm-up calls, then exactly K calls captured in one HIP graph
-and replayed once between two events on the launch stream, with
-synchronisation on both sides.  Inputs rotate over enough copies that the
+Timing: W eager warm-up calls (extended to ~0.3 s so clocks settle), then
+exactly K calls between two events on the launch stream, with synchronisation
+on both sides: replayed from one HIP graph when a call is launch-bound (under
+20 us), plain back-to-back launches otherwise.  Inputs rotate over enough copies that the
 working set exceeds the 256 MB MALL (cold, as a serving step sees per-layer
 KV); --hot keeps one copy.
 
@@ -27,6 +28,7 @@ import argparse
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -49,6 +51,13 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--tunables", default="",
                     help="launch overrides, e.g. rows_per_block=3,split_kv=64 (0 = heuristic)")
+    ap.add_argument("--write-traffic-profile", nargs=6, default=None,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
+                             "CAL_MIB"),
+                    help="summarise FETCH_SIZE/WRITE_SIZE runs into profiles/ (no GPU needed)")
+    ap.add_argument("--write-kernel-stats", nargs=2, default=None, metavar=("WORKLOAD", "STATS_DIR"),
+                    help="summarise a rocprofv3 --stats run into profiles/ (no GPU needed)")
+    ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -116,7 +125,7 @@ class Workload:
                                     self.host.max_model_len, logits=out, tunables=self.tun)
 
 
-def time_workload(wl, steps, warmup, graph=True, settle_s=0.3):
+def time_workload(wl, steps, warmup, graph=None, settle_s=0.3):
     """Per-call milliseconds of exactly `steps` calls.  Warm-up: `warmup`
     calls, extended until about settle_s of GPU work has run so that clocks
     have left their idle state before the timed region."""
@@ -131,6 +140,19 @@ def time_workload(wl, steps, warmup, graph=True, settle_s=0.3):
     torch.cuda.synchronize()
     wl.warmup_done = i
     stream = torch.cuda.current_stream()
+    if graph is None:
+        # Launch-bound calls (a few microseconds) are replayed from a HIP graph;
+        # longer ones are timed as plain back-to-back launches, which keeps the
+        # host's launch gap inside the measurement.
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(8):
+            wl.call(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph = e0.elapsed_time(e1) / 8 < 0.02
+    wl.graph = graph
     if graph:
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -160,6 +182,7 @@ def time_workload(wl, steps, warmup, graph=True, settle_s=0.3):
 def summarize(wl, ms):
     us = ms * 1e3
     d = dict(workload=wl.cfg["name"], us_per_call=round(us, 3), input_copies=wl.nsets,
+             timing="hip graph replay" if wl.graph else "back-to-back launches",
              essential_bytes=int(wl.bytes), valid_pairs=int(wl.pairs))
     tbs = wl.bytes / (ms * 1e-3) / 1e12
     tflops = wl.flops / (ms * 1e-3) / 1e12
@@ -217,8 +240,107 @@ def calib_copy(mib):
     print(json.dumps({"calib_copy_bytes": n, "reads": n, "writes": n}))
 
 
+PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def source_hash():
+    """Hash of the kernel sources and device build flags: a traffic profile is
+    only reported while it matches the code being timed."""
+    import hashlib
+    from sparse_attention_indexer_scaled_amd import build
+    h = hashlib.sha256(" ".join(build.DEVICE).encode())
+    for name in sorted(os.listdir(build.CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(build.CSRC, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_avg(csv_dir, counter, name_part):
+    """Per-dispatch average of one counter over dispatches whose kernel name
+    contains name_part (rocprofv3 --pmc ... --output-format csv)."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                key = (path, r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s samples for %r under %s" % (counter, name_part, csv_dir))
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def write_traffic_profile(workload_name, kernel_part, fetch_dir, write_dir, cal_fetch_dir,
+                          cal_write_dir, cal_bytes, command):
+    fetch, nf = _pmc_avg(fetch_dir, "FETCH_SIZE", kernel_part)
+    write, nw_ = _pmc_avg(write_dir, "WRITE_SIZE", kernel_part)
+    cfetch, _ = _pmc_avg(cal_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cwrite, _ = _pmc_avg(cal_write_dir, "WRITE_SIZE", "copyBuffer")
+    fetch_factor = cal_bytes / (cfetch * 1024)
+    write_factor = cal_bytes / (cwrite * 1024)
+    out = {"workload": workload_name, "kernel": kernel_part, "source_hash": source_hash(),
+           "fetch_kib_per_dispatch": round(fetch, 1), "write_kib_per_dispatch": round(write, 1),
+           "dispatches": [nf, nw_],
+           "calibration": {"copy_bytes": cal_bytes, "fetch_kib": round(cfetch, 1),
+                           "write_kib": round(cwrite, 1), "fetch_factor": round(fetch_factor, 4),
+                           "write_factor": round(write_factor, 4)},
+           "hbm_read_bytes": int(fetch * 1024 * fetch_factor),
+           "hbm_write_bytes": int(write * 1024 * write_factor),
+           "command": command}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    path = os.path.join(PROFILE_DIR, "%s_traffic.json" % workload_name)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(path)
+
+
+def write_kernel_stats(workload_name, stats_dir, command):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit("no kernel_stats.csv under %s" % stats_dir)
+    rows = list(csv.DictReader(open(paths[0])))
+    lines = ["# rocprofv3 kernel statistics: %s" % workload_name,
+             "# command: %s" % command, "# source_hash: %s" % source_hash(),
+             "name | calls | average_ns | min_ns | max_ns | percent"]
+    for r in rows:
+        m = re.match(r"(.*?>)\(", r["Name"])
+        name = m.group(1) if m else r["Name"].split("(")[0]
+        lines.append("%s | %s | %.1f | %s | %s | %s" % (name, r["Calls"], float(r["AverageNs"]),
+                                                         r["MinNs"], r["MaxNs"], r["Percentage"]))
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    path = os.path.join(PROFILE_DIR, "%s_kernel_stats.txt" % workload_name)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def read_traffic(workload_name):
+    path = os.path.join(PROFILE_DIR, "%s_traffic.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t["hbm_read_bytes"] + t["hbm_write_bytes"]
+
+
 def main():
     args = parse()
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    if args.write_traffic_profile:
+        w, fd, wd, cfd, cwd, mib = args.write_traffic_profile
+        kernel = "decode_kernel" if w.startswith("decode") else "prefill_kernel"
+        write_traffic_profile(w, kernel, fd, wd, cfd, cwd, int(mib) << 20, args.profile_command)
+        return
+    if args.write_kernel_stats:
+        write_kernel_stats(args.write_kernel_stats[0], args.write_kernel_stats[1], args.profile_command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the op needs no exchange between GPUs; see DESIGN.md)", file=sys.stderr)
@@ -241,7 +363,7 @@ def main():
     results, head = {}, None
     for idx in order:
         wl = Workload(idx, args.hot, tun)
-        ms = time_workload(wl, args.steps, args.warmup, graph=not args.no_graph)
+        ms = time_workload(wl, args.steps, args.warmup, graph=False if args.no_graph else None)
         results[wl.cfg["name"]] = summarize(wl, ms)
         print("[bench] %s: %.2f us/call" % (wl.cfg["name"], ms * 1e3), file=sys.stderr, flush=True)
         if idx == order[0]:
@@ -275,9 +397,10 @@ def main():
                     "cold": not args.hot}),
         "roofline": ({"bound": "hbm", "achieved": round(r["essential_TBps"] * 1e3, 2),
                       "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s", "frac": r["hbm_frac"],
-                      "traffic": None} if decode else
+                      "traffic": read_traffic(wl.cfg["name"])} if decode else
                      {"bound": "mfma", "achieved": r["fp8_TFLOPs"], "peak": FP8_PEAK_TFLOPS,
-                      "unit": "TFLOP/s", "frac": r["mfma_frac"], "traffic": None}),
+                      "unit": "TFLOP/s", "frac": r["mfma_frac"],
+                      "traffic": read_traffic(wl.cfg["name"])}),
         "workloads": results,
     }
     if not args.no_cpu and decode:

@@ -148,12 +148,16 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     p.M = M;
     p.N = N;
     p.clean = clean_logits ? 1 : 0;
-    // Heuristic: 4 rows per wave share each K step; 4 waves per workgroup split
-    // the columns; enough column splits that the grid holds ~2048 workgroups
-    // while each wave still gets >= 4 steps; high-m first for long causal
-    // chunks (aiter PR 5046 page, "Technical Details": N > 2048).
-    p.block_m = t.block_m ? t.block_m : 4;
-    p.num_warps = t.num_warps ? t.num_warps : 4;
+    // Heuristic (measured on MI355X; both pages, "Technical Details", make
+    // the row block, split and wave count host-chosen): for long chunks 8 rows
+    // per wave share each K step (1 wave per SIMD; K is re-read per row block
+    // from L2, so a larger block means less L2 traffic) with one wave per
+    // workgroup; short chunks take 4 rows and 4 waves for parallelism; and
+    // enough column splits for ~2048 workgroups while each wave keeps >= 4
+    // steps.  High-m first for long causal chunks (aiter PR 5046 page,
+    // "Technical Details": N > 2048).
+    p.block_m = t.block_m ? t.block_m : (M >= 1024 ? 8 : 4);
+    p.num_warps = t.num_warps ? t.num_warps : (M >= 1024 ? 1 : 4);
     const int64_t nrb = ceil_div(M, p.block_m);
     const int64_t steps = ceil_div(N, 64);
     if (t.split_n) {
@@ -223,13 +227,14 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     // Heuristic (aiter PR 5047 page, "Technical Details": rows per K stream and
     // the KV split are chosen on the host from batch * max_model_len, since the
     // device-resident context lengths are not visible without a sync).
-    //   rows: all next_n rows share one wave's K stream up to 4 (Q + weights
-    //         = 32 VGPR per row); above that two row groups (e.g. 6 -> 2 x 3)
-    //         whose waves walk the same blocks side by side (L1 hits).
-    //   waves: 4 waves per workgroup (measured better than 8); a workgroup
-    //         may hold up to 8 while a wave fits 256 registers, 4 beyond.
-    //   split: ~2 workgroups per CU in total, but at least 2 steps per wave.
-    int rows = t.rows_per_block ? t.rows_per_block : (next_n <= 4 ? next_n : (next_n + 1) / 2);
+    // Measured on MI355X:
+    //   rows: all next_n rows share one wave's K stream (K read once); above
+    //         4 rows a wave needs more than 256 registers (1 wave per SIMD).
+    //   waves: 4 K streams per workgroup.
+    //   split: about one workgroup per CU in total when a wave holds more than
+    //         4 rows, 2048 workgroups otherwise (many short work items balance
+    //         ragged batches), but at least 2 steps per wave.
+    int rows = t.rows_per_block ? t.rows_per_block : next_n;
     rows = std::min(rows, next_n);
     p.rows = rows;
     const int groups = (next_n + rows - 1) / rows;
@@ -245,7 +250,8 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     if (t.split_kv) {
         p.split_kv = t.split_kv;
     } else {
-        const int64_t want = ceil_div(512, batch);
+        const int64_t target = rows > 4 ? 256 : 2048;
+        const int64_t want = ceil_div(target, batch);
         const int64_t cap = std::max<int64_t>(1, steps_max / (2 * p.num_warps));
         p.split_kv = (int)std::max<int64_t>(1, std::min(want, cap));
     }

@@ -66,16 +66,29 @@ template <int BM>
 __device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[BM],
                                             const Weights16 (&w)[BM], float (&tot)[2][(BM + 1) / 2])
 {
+    // Row-tiles in the order (tile 0: rows 0..BM-1, tile 1: rows 0..BM-1), software
+    // pipelined by one: the MFMAs of row-tile i+1 are issued before the
+    // relu.weight epilogue of row-tile i, so the epilogue never waits for the
+    // MFMA it consumes and the matrix core has work queued meanwhile.
+    constexpr int NT = 2 * BM;
+    float part[2][BM];
+    f32x16 prev = row_scores(q[0], k.t[0]);
+#pragma unroll
+    for (int it = 1; it < NT; ++it) {
+        const int h = it / BM, r = it % BM;
+        const int ph = (it - 1) / BM, pr = (it - 1) % BM;
+        f32x16 cur = row_scores(q[r], k.t[h]);
+        part[ph][pr] = relu_weight_sum(prev, w[pr]);
+        prev = cur;
+    }
+    part[1][BM - 1] = relu_weight_sum(prev, w[BM - 1]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        float part[BM];
-#pragma unroll
-        for (int r = 0; r < BM; ++r)
-            part[r] = relu_weight_sum(row_scores(q[r], k.t[h]), w[r]);
 #pragma unroll
         for (int i = 0; i < (BM + 1) / 2; ++i) {
-            const float pb = (2 * i + 1 < BM) ? part[(2 * i + 1 < BM) ? 2 * i + 1 : 2 * i] : part[2 * i];
-            tot[h][i] = pair_head_sum(part[2 * i], pb) * k.sc[h];
+            // an odd last row is paired with itself; its upper half is never stored
+            const float pb = (2 * i + 1 < BM) ? part[h][(2 * i + 1 < BM) ? 2 * i + 1 : 2 * i] : part[h][2 * i];
+            tot[h][i] = pair_head_sum(part[h][2 * i], pb) * k.sc[h];
         }
     }
 }
