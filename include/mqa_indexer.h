@@ -58,12 +58,13 @@ extern "C" {
  *     num_warps    waves per workgroup (they split the column range), 1..4
  *     reverse_rows 1 = dispatch row blocks high-m first, -1 = natural order
  *   decode:
- *     rows_per_block  next_n rows that share one K stream per wave, 1..8
- *                     (clamped to next_n); ceil(next_n / rows_per_block)
- *                     row-group waves walk each K stream side by side
+ *     rows_per_block  next_n rows each wave computes, 1..4 (clamped to
+ *                     next_n); a workgroup has ceil(next_n / rows_per_block)
+ *                     such waves, all fed from one K stream
  *     split_kv        workgroups per sequence along KV, >= 1
- *     num_warps       K streams per workgroup; num_warps x row groups must
- *                     not exceed 8 waves (4 when rows_per_block > 4)
+ *     ring_depth      cache blocks each workgroup keeps in its LDS ring
+ *                     (requests run ring_depth - 1 blocks ahead), 2..7
+ *     (num_warps must be 0 for decode)
  */
 typedef struct mqa_tunables {
     int block_m;
@@ -72,6 +73,7 @@ typedef struct mqa_tunables {
     int reverse_rows;
     int rows_per_block;
     int split_kv;
+    int ring_depth;
 } mqa_tunables;
 
 /*

@@ -36,7 +36,8 @@ class Tunables(ctypes.Structure):
     """mqa_tunables: 0 in a field means the host heuristic chooses."""
     _fields_ = [("block_m", ctypes.c_int), ("split_n", ctypes.c_int),
                 ("num_warps", ctypes.c_int), ("reverse_rows", ctypes.c_int),
-                ("rows_per_block", ctypes.c_int), ("split_kv", ctypes.c_int)]
+                ("rows_per_block", ctypes.c_int), ("split_kv", ctypes.c_int),
+                ("ring_depth", ctypes.c_int)]
 
 
 _lib = None

@@ -199,9 +199,11 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     mqa_tunables t = {};
     if (tun)
         t = *tun;
-    if (t.rows_per_block < 0 || t.rows_per_block > 8 || t.split_kv < 0 || t.num_warps < 0 ||
-        t.num_warps > 8)
-        return fail(MQA_ERR_INVALID_ARG, "rows_per_block in 0..8, split_kv >= 0, num_warps in 0..8");
+    if (t.rows_per_block < 0 || t.rows_per_block > 4 || t.split_kv < 0 || t.num_warps != 0 ||
+        t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7)
+        return fail(MQA_ERR_INVALID_ARG,
+                    "decode tunables: rows_per_block in 0..4, split_kv >= 0, ring_depth 0 or 2..7, "
+                    "num_warps 0");
     if (batch == 0 || max_model_len == 0)
         return ok();
     if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables || !logits)
@@ -228,38 +230,30 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     // the KV split are chosen on the host from batch * max_model_len, since the
     // device-resident context lengths are not visible without a sync).
     // Measured on MI355X:
-    //   rows: all next_n rows share one wave's K stream (K read once); above
-    //         4 rows a wave needs more than 256 registers (1 wave per SIMD).
-    //   waves: 4 K streams per workgroup.
-    //   split: about one workgroup per CU in total when a wave holds more than
-    //         4 rows, 2048 workgroups otherwise (many short work items balance
-    //         ragged batches), but at least 2 steps per wave.
-    int rows = t.rows_per_block ? t.rows_per_block : next_n;
+    //   rows: every wave of a workgroup reads the same LDS ring, so all next_n
+    //         rows share one HBM stream whatever the row split; 2 waves per
+    //         workgroup (e.g. next_n 6 -> 2 x 3 rows) keep each wave within 256
+    //         registers, 2 waves per SIMD.
+    //   depth: 4 blocks (33 KiB) per workgroup, 4 workgroups per CU.
+    //   split: at least ~1024 workgroups, and at most 32 steps (2048 tokens)
+    //          per workgroup at the longest context, but at least 4 steps.
+    int rows = t.rows_per_block ? t.rows_per_block : (next_n == 1 ? 1 : (next_n + 1) / 2);
     rows = std::min(rows, next_n);
     p.rows = rows;
-    const int groups = (next_n + rows - 1) / rows;
-    const int max_waves = rows <= 4 ? 8 : 4;
-    if (groups > max_waves)
-        return fail(MQA_ERR_INVALID_ARG, "rows_per_block=%d gives %d row groups; at most %d fit a workgroup",
-                    rows, groups, max_waves);
-    p.num_warps = t.num_warps ? t.num_warps : std::max(1, 4 / groups);
-    if (p.num_warps * groups > max_waves)
-        return fail(MQA_ERR_INVALID_ARG, "num_warps=%d x %d row groups exceeds %d waves per workgroup",
-                    p.num_warps, groups, max_waves);
+    p.depth = t.ring_depth ? t.ring_depth : 4;
     const int64_t steps_max = ceil_div(max_model_len, 64);
     if (t.split_kv) {
         p.split_kv = t.split_kv;
     } else {
-        const int64_t target = rows > 4 ? 256 : 2048;
-        const int64_t want = ceil_div(target, batch);
-        const int64_t cap = std::max<int64_t>(1, steps_max / (2 * p.num_warps));
+        const int64_t want = std::max(ceil_div(1024, batch), ceil_div(steps_max, 32));
+        const int64_t cap = std::max<int64_t>(1, steps_max / 4);
         p.split_kv = (int)std::max<int64_t>(1, std::min(want, cap));
     }
     if ((int64_t)batch * p.split_kv > INT32_MAX)
         return fail(MQA_ERR_INVALID_ARG, "grid too large");
     if (trace_on())
-        std::fprintf(stderr, "[mqa] decode B=%d next_n=%d mml=%d rows=%d split_kv=%d warps=%d\n", batch,
-                     next_n, max_model_len, p.rows, p.split_kv, p.num_warps);
+        std::fprintf(stderr, "[mqa] decode B=%d next_n=%d mml=%d rows=%d split_kv=%d depth=%d\n", batch,
+                     next_n, max_model_len, p.rows, p.split_kv, p.depth);
     hipError_t e = mqa::launch_decode(p, stream);
     if (e != hipSuccess)
         return fail(MQA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));

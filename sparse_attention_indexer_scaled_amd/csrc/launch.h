@@ -36,10 +36,13 @@ struct DecodeLaunch {
     int max_blocks_per_seq;
     int64_t max_model_len;
     int clean;
-    int rows;      // rows per wave (R), 1..8, <= next_n
-    int split_kv;  // workgroups per (sequence, row group)
-    int num_warps; // waves per workgroup
+    int rows;      // rows per wave (R), 1..4, <= next_n; ceil(next_n / R) waves per workgroup
+    int split_kv;  // workgroups per sequence
+    int depth;     // cache blocks in each workgroup's LDS ring, 2..7 (at most 64 KiB)
 };
+
+// Bytes of LDS a decode workgroup uses for a ring of `depth` blocks.
+int decode_ring_bytes(int depth);
 
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);

@@ -118,8 +118,10 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls) == mqa._native.MQA_ERR_INVALID_ARG
     odd = [P(0x2002)] * 6
     assert _decode(lib, odd) == mqa._native.MQA_ERR_INVALID_ARG
-    bad = _native.Tunables(rows_per_block=9)
-    assert _decode(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    for bad in (_native.Tunables(rows_per_block=5), _native.Tunables(ring_depth=1),
+                _native.Tunables(ring_depth=8), _native.Tunables(num_warps=2),
+                _native.Tunables(split_kv=-1)):
+        assert _decode(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
 
 
 def test_binding_raises_on_missing_library(tmp_path):

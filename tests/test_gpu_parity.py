@@ -136,15 +136,40 @@ def test_decode_matches_oracle(B, next_n, ctx, mml, clean):
         assert_parity(np.where(win, out, -np.inf), ref, mag, f"decode_B{B}_nn{next_n}_noclean")
 
 
-@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_decode_every_row_grouping(rows):
-    """Every rows-per-wave instantiation, including groups that do not divide
-    next_n (the last group is short)."""
-    d = inputs.make_decode(2, 8, [900, 77], 1000, seed=300 + rows, poison=True)
-    say("decode rows_per_block=%d" % rows)
+def _row_instantiations():
+    """(next_n, rows_per_block) pairs reaching every (rows per wave, waves per
+    workgroup) kernel instantiation once."""
+    seen, out = set(), []
+    for nn in range(1, 9):
+        for rows in range(1, min(4, nn) + 1):
+            key = (rows, -(-nn // rows))
+            if key not in seen:
+                seen.add(key)
+                out.append((nn, rows))
+    return out
+
+
+@pytest.mark.parametrize("next_n,rows", _row_instantiations())
+def test_decode_every_row_grouping(next_n, rows):
+    """Every rows-per-wave x waves-per-workgroup instantiation, including row
+    groups that do not divide next_n (the last wave of the workgroup is short)."""
+    d = inputs.make_decode(2, next_n, [900, 77], 1000, seed=300 + 10 * next_n + rows, poison=True)
+    say("decode next_n=%d rows_per_block=%d" % (next_n, rows))
     out = run_decode(d, tun=Tunables(rows_per_block=rows))
     ref, mag, _ = oracle_decode(d)
-    assert_parity(out, ref, mag, f"decode_rows{rows}")
+    assert_parity(out, ref, mag, f"decode_nn{next_n}_rows{rows}")
+
+
+@pytest.mark.parametrize("depth", [2, 3, 5, 7])
+def test_decode_every_ring_depth(depth):
+    """LDS ring depths other than the default, with splits that leave some
+    workgroups fewer steps than the ring holds."""
+    d = inputs.make_decode(3, 5, [700, 130, 3000], 3072, seed=310 + depth, poison=True)
+    say("decode ring_depth=%d" % depth)
+    for split in (1, 7):
+        out = run_decode(d, tun=Tunables(ring_depth=depth, split_kv=split))
+        ref, mag, _ = oracle_decode(d)
+        assert_parity(out, ref, mag, f"decode_depth{depth}_split{split}")
 
 
 # ---------------------------------------------------------------------------
@@ -165,9 +190,10 @@ def test_prefill_tunables_do_not_change_bits():
 def test_decode_tunables_do_not_change_bits():
     d = inputs.make_decode(3, 6, [2000, 150, 1300], 2048, seed=402, poison=True)
     base = run_decode(d)
-    for tun in [Tunables(rows_per_block=1), Tunables(rows_per_block=6, split_kv=1),
-                Tunables(rows_per_block=3, split_kv=9, num_warps=1), Tunables(split_kv=64),
-                Tunables(rows_per_block=4, num_warps=2), Tunables(rows_per_block=6, num_warps=4, split_kv=3), Tunables(rows_per_block=2, split_kv=5, num_warps=2)]:
+    for tun in [Tunables(rows_per_block=1), Tunables(rows_per_block=4, split_kv=1),
+                Tunables(rows_per_block=3, split_kv=9, ring_depth=2), Tunables(split_kv=64),
+                Tunables(rows_per_block=2, ring_depth=7), Tunables(rows_per_block=4, split_kv=3, ring_depth=3),
+                Tunables(rows_per_block=2, split_kv=5)]:
         say("decode tunables %s" % [getattr(tun, f) for f, _ in Tunables._fields_])
         assert np.array_equal(run_decode(d, tun=tun), base, equal_nan=True)
 
