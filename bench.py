@@ -57,6 +57,10 @@ def parse():
                     help="summarise FETCH_SIZE/WRITE_SIZE runs into profiles/ (no GPU needed)")
     ap.add_argument("--write-kernel-stats", nargs=2, default=None, metavar=("WORKLOAD", "STATS_DIR"),
                     help="summarise a rocprofv3 --stats run into profiles/ (no GPU needed)")
+    ap.add_argument("--write-counter-profile", nargs="+", default=None,
+                    metavar="WORKLOAD_OR_DIR",
+                    help="WORKLOAD DIR [DIR ...]: summarise rocprofv3 --pmc runs of SQ/GRBM "
+                         "counters into profiles/ (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -243,17 +247,27 @@ def calib_copy(mib):
 PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
-def source_hash():
-    """Hash of the kernel sources and device build flags: a traffic profile is
-    only reported while it matches the code being timed."""
+KERNEL_SOURCES = {
+    "decode_kernel": ("device.h", "launch.h", "api.cpp", "decode.hip"),
+    "prefill_kernel": ("device.h", "launch.h", "api.cpp", "prefill.hip"),
+}
+
+
+def source_hash(kernel):
+    """Hash of one kernel's sources (with the host launcher that picks its
+    launch shape) and the device build flags: a profile is only reported while
+    it matches the code being timed."""
     import hashlib
     from sparse_attention_indexer_scaled_amd import build
     h = hashlib.sha256(" ".join(build.DEVICE).encode())
-    for name in sorted(os.listdir(build.CSRC)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            with open(os.path.join(build.CSRC, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(build.CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_of(workload_name):
+    return "decode_kernel" if workload_name.startswith("decode") else "prefill_kernel"
 
 
 def _pmc_avg(csv_dir, counter, name_part):
@@ -280,7 +294,7 @@ def write_traffic_profile(workload_name, kernel_part, fetch_dir, write_dir, cal_
     cwrite, _ = _pmc_avg(cal_write_dir, "WRITE_SIZE", "copyBuffer")
     fetch_factor = cal_bytes / (cfetch * 1024)
     write_factor = cal_bytes / (cwrite * 1024)
-    out = {"workload": workload_name, "kernel": kernel_part, "source_hash": source_hash(),
+    out = {"workload": workload_name, "kernel": kernel_part, "source_hash": source_hash(kernel_part),
            "fetch_kib_per_dispatch": round(fetch, 1), "write_kib_per_dispatch": round(write, 1),
            "dispatches": [nf, nw_],
            "calibration": {"copy_bytes": cal_bytes, "fetch_kib": round(cfetch, 1),
@@ -305,7 +319,8 @@ def write_kernel_stats(workload_name, stats_dir, command):
         raise SystemExit("no kernel_stats.csv under %s" % stats_dir)
     rows = list(csv.DictReader(open(paths[0])))
     lines = ["# rocprofv3 kernel statistics: %s" % workload_name,
-             "# command: %s" % command, "# source_hash: %s" % source_hash(),
+             "# command: %s" % command,
+             "# source_hash: %s" % source_hash(kernel_of(workload_name)),
              "name | calls | average_ns | min_ns | max_ns | percent"]
     for r in rows:
         m = re.match(r"(.*?>)\(", r["Name"])
@@ -319,13 +334,81 @@ def write_kernel_stats(workload_name, stats_dir, command):
     print(path)
 
 
+NUM_SIMDS = 256 * 4   # MI355X: 256 CUs x 4 SIMDs
+NUM_XCDS = 8          # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+
+
+def _pmc_dispatches(csv_dir, name_part):
+    """{(file, dispatch): {"ns": duration, counter: value}} for dispatches whose
+    kernel name contains name_part."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if name_part not in r["Kernel_Name"]:
+                continue
+            d = out.setdefault((path, r["Dispatch_Id"]), {})
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def write_counter_profile(workload_name, kernel_part, dirs, command):
+    """Per-dispatch averages of SQ/GRBM counters over one or more rocprofv3
+    --pmc runs, and what they say about the MFMA and VALU pipes."""
+    avg, durations = {}, []
+    for d in dirs:
+        disp = _pmc_dispatches(d, kernel_part)
+        if not disp:
+            raise SystemExit("no samples for %r under %s" % (kernel_part, d))
+        durations += [v["ns"] for v in disp.values()]
+        for name in {k for v in disp.values() for k in v if k != "ns"}:
+            vals = [v[name] for v in disp.values() if name in v]
+            avg[name] = sum(vals) / len(vals)
+    out = {"workload": workload_name, "kernel": kernel_part, "source_hash": source_hash(kernel_part),
+           "dispatches": len(durations),
+           "median_dispatch_us": round(sorted(durations)[len(durations) // 2] / 1e3, 3),
+           "counters_per_dispatch": {k: round(v, 1) for k, v in sorted(avg.items())},
+           "command": command}
+    derived = {}
+    gui = avg.get("GRBM_GUI_ACTIVE")
+    if gui:
+        simd_cycles = NUM_SIMDS * gui / NUM_XCDS
+        derived["clock_GHz"] = round(gui / NUM_XCDS / (out["median_dispatch_us"] * 1e3), 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            derived["mfma_busy_frac"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles, 4)
+        if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+            derived["non_mfma_valu_insts"] = int(avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"])
+    if "SQ_INSTS_VALU_MFMA_MOPS_F8" in avg:
+        # one MOPS unit is 512 flops
+        derived["mfma_fp8_flops"] = int(avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512)
+    out["derived"] = derived
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    path = os.path.join(PROFILE_DIR, "%s_counters.json" % workload_name)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(path)
+
+
+def read_counters(workload_name):
+    path = os.path.join(PROFILE_DIR, "%s_counters.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash(kernel_of(workload_name)):
+        return None
+    return t["derived"]
+
+
 def read_traffic(workload_name):
     path = os.path.join(PROFILE_DIR, "%s_traffic.json" % workload_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash(kernel_of(workload_name)):
         return None
     return t["hbm_read_bytes"] + t["hbm_write_bytes"]
 
@@ -335,8 +418,13 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     if args.write_traffic_profile:
         w, fd, wd, cfd, cwd, mib = args.write_traffic_profile
-        kernel = "decode_kernel" if w.startswith("decode") else "prefill_kernel"
+        kernel = kernel_of(w)
         write_traffic_profile(w, kernel, fd, wd, cfd, cwd, int(mib) << 20, args.profile_command)
+        return
+    if args.write_counter_profile:
+        w, dirs = args.write_counter_profile[0], args.write_counter_profile[1:]
+        kernel = kernel_of(w)
+        write_counter_profile(w, kernel, dirs, args.profile_command)
         return
     if args.write_kernel_stats:
         write_kernel_stats(args.write_kernel_stats[0], args.write_kernel_stats[1], args.profile_command)
@@ -365,6 +453,9 @@ def main():
         wl = Workload(idx, args.hot, tun)
         ms = time_workload(wl, args.steps, args.warmup, graph=False if args.no_graph else None)
         results[wl.cfg["name"]] = summarize(wl, ms)
+        counters = read_counters(wl.cfg["name"])
+        if counters:
+            results[wl.cfg["name"]]["counters"] = counters
         print("[bench] %s: %.2f us/call" % (wl.cfg["name"], ms * 1e3), file=sys.stderr, flush=True)
         if idx == order[0]:
             head = (wl, ms)
