@@ -9,6 +9,8 @@ Python side of ``oracle/mqa_oracle.c`` (plain fp64 C, OpenMP over rows).  See
 that file for the definition, the window rules and the exactness argument.
 Inputs are numpy arrays in the op's own layouts; outputs are float64.
 
+The row-wise top-k that consumes the logits is in ``oracle.topk`` (numpy).
+
 Every function here is pinned by the ``-m "not gpu"`` tests against things
 other than itself: an exact rational brute force (``oracle.brute``), numpy
 matmul closed forms, the fp8 table of torch's own e4m3fn conversion, and the
