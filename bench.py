@@ -78,6 +78,11 @@ def cpu_model():
     return platform.processor()
 
 
+# Top-k workloads: index -> (decode workload whose logits are ranked, k).  The
+# pages' deployments use index_topk 2048 and 512.
+TOPK_WORKLOADS = {5: (2, 2048), 6: (2, 512)}
+
+
 class Workload:
     """Device-resident input copies and output buffers for one named workload."""
 
@@ -127,6 +132,46 @@ class Workload:
         else:
             paged_mqa_logits_decode(s["q"], s["cache"], s["w"], s["ctx"], s["bt"],
                                     self.host.max_model_len, logits=out, tunables=self.tun)
+
+
+class TopkWorkload:
+    """Row-wise top-k over the logits of a decode workload (the indexer's
+    consumer).  The logits are produced once by the decode kernel, then copied
+    so that the timed calls rotate over > COLD_BYTES of input."""
+
+    def __init__(self, idx, hot):
+        import torch
+        decode_idx, k = TOPK_WORKLOADS[idx]
+        src = Workload(decode_idx, True)
+        src.call(0)
+        torch.cuda.synchronize()
+        logits = src.outs[0]
+        rows, cols = logits.shape
+        self.idx = idx
+        self.kind = "topk"
+        self.k = k
+        self.cfg = {"kind": "topk", "name": "topk_k%d_%s" % (k, src.cfg["name"]),
+                    "rows": rows, "cols": cols, "k": k}
+        self.host = src.host
+        self.bytes = rows * cols * 4 + rows * k * 4
+        self.pairs = 0
+        self.flops = 0
+        set_bytes = rows * cols * 4
+        nsets = 1 if hot else min(64, max(1, -(-COLD_BYTES // set_bytes)))
+        self.sets = [logits] + [logits.clone() for _ in range(nsets - 1)]
+        self.outs = [torch.empty((rows, k), dtype=torch.int32, device="cuda") for _ in range(nsets)]
+        self.nsets = nsets
+        del src
+
+    def call(self, i):
+        from sparse_attention_indexer_scaled_amd import topk_indices
+        topk_indices(self.sets[i % self.nsets], self.k, indices=self.outs[i % self.nsets])
+
+
+def make_workload(idx, hot, tunables=None):
+    if idx in TOPK_WORKLOADS:
+        return TopkWorkload(idx, hot)
+    return Workload(idx, hot, tunables)
 
 
 def time_workload(wl, steps, warmup, graph=None, settle_s=0.3):
@@ -192,8 +237,9 @@ def summarize(wl, ms):
     tflops = wl.flops / (ms * 1e-3) / 1e12
     d["essential_TBps"] = round(tbs, 4)
     d["hbm_frac"] = round(tbs / HBM_PEAK_TBS, 4)
-    d["fp8_TFLOPs"] = round(tflops, 2)
-    d["mfma_frac"] = round(tflops / FP8_PEAK_TFLOPS, 4)
+    if wl.flops:
+        d["fp8_TFLOPs"] = round(tflops, 2)
+        d["mfma_frac"] = round(tflops / FP8_PEAK_TFLOPS, 4)
     return d
 
 
@@ -250,6 +296,7 @@ PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles
 KERNEL_SOURCES = {
     "decode_kernel": ("device.h", "launch.h", "api.cpp", "decode.hip"),
     "prefill_kernel": ("device.h", "launch.h", "api.cpp", "prefill.hip"),
+    "topk_kernel": ("launch.h", "api.cpp", "topk.hip"),
 }
 
 
@@ -267,7 +314,10 @@ def source_hash(kernel):
 
 
 def kernel_of(workload_name):
-    return "decode_kernel" if workload_name.startswith("decode") else "prefill_kernel"
+    for prefix in ("decode", "prefill", "topk"):
+        if workload_name.startswith(prefix):
+            return prefix + "_kernel"
+    raise ValueError(workload_name)
 
 
 def _pmc_avg(csv_dir, counter, name_part):
@@ -447,10 +497,10 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6) if i != args.workload]
     results, head = {}, None
     for idx in order:
-        wl = Workload(idx, args.hot, tun)
+        wl = make_workload(idx, args.hot, tun)
         ms = time_workload(wl, args.steps, args.warmup, graph=False if args.no_graph else None)
         results[wl.cfg["name"]] = summarize(wl, ms)
         counters = read_counters(wl.cfg["name"])
@@ -467,10 +517,21 @@ def main():
     r = results[wl.cfg["name"]]
     h = wl.host
     decode = wl.kind == "decode"
+    hbm_bound = wl.kind in ("decode", "topk")
+    if wl.kind == "topk":
+        config = {"workload": wl.cfg["name"], "rows": wl.cfg["rows"], "cols": wl.cfg["cols"],
+                  "k": wl.k, "cold": not args.hot}
+    elif decode:
+        config = {"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
+                  "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
+                  "heads": 32, "head_dim": 128, "kv_block_size": 64, "cold": not args.hot}
+    else:
+        config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": 32, "head_dim": 128,
+                  "cold": not args.hot}
     line = {
         "metric": "decode essential HBM TB/s (% of 8 TB/s); prefill fp8 TFLOP/s; us/call",
-        "value": r["essential_TBps"] if decode else r["fp8_TFLOPs"],
-        "unit": "TB/s" if decode else "TFLOP/s",
+        "value": r["essential_TBps"] if hbm_bound else r["fp8_TFLOPs"],
+        "unit": "TB/s" if hbm_bound else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": wl.warmup_done,
@@ -480,15 +541,10 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8e4m3 (fp32 accumulate)",
         "data": "synthetic (seeded; N(0,1) Q/K, per-token fp8 K scale, random block table)",
-        "config": ({"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
-                    "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
-                    "heads": 32, "head_dim": 128, "kv_block_size": 64, "cold": not args.hot}
-                   if decode else
-                   {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": 32, "head_dim": 128,
-                    "cold": not args.hot}),
+        "config": config,
         "roofline": ({"bound": "hbm", "achieved": round(r["essential_TBps"] * 1e3, 2),
                       "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s", "frac": r["hbm_frac"],
-                      "traffic": read_traffic(wl.cfg["name"])} if decode else
+                      "traffic": read_traffic(wl.cfg["name"])} if hbm_bound else
                      {"bound": "mfma", "achieved": r["fp8_TFLOPs"], "peak": FP8_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": r["mfma_frac"],
                       "traffic": read_traffic(wl.cfg["name"])}),

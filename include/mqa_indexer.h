@@ -154,6 +154,26 @@ int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const
                             int max_model_len, int clean_logits, const mqa_tunables *tun,
                             hipStream_t stream);
 
+/*
+ * Row-wise top-k of a logits matrix: the selection that consumes the indexer
+ * (index_topk 2048 or 512 on the aiter PR 5047 page, "Integration" and the
+ * serving notes; the issue page about next_n tiling, "Setup").  The pages do
+ * not define the selection order; this call uses one total order:
+ *
+ *   logits   [rows, cols]  fp32, 4-byte aligned
+ *   indices  [rows, k]     int32, written
+ *
+ * Row r's output lists column indices by decreasing value, equal values by
+ * increasing column; -inf and NaN entries are never listed (so the -inf
+ * written outside each window by clean_logits = 1 excludes those positions);
+ * -0.0 counts as equal to +0.0.  When a row has fewer than k listable entries
+ * the rest of its output is -1.  1 <= k <= 2048.
+ * rows == 0 is a successful no-op; cols == 0 writes all -1.  Negative sizes, k
+ * out of range, NULL or misaligned pointers -> MQA_ERR_INVALID_ARG.
+ */
+int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *indices,
+                     hipStream_t stream);
+
 /* Human-readable reason for this thread's last non-zero return ("" if none). */
 const char *mqa_last_error(void);
 

@@ -20,4 +20,5 @@ from ._native import (  # noqa: F401
     load_library,
     mqa_logits_prefill,
     paged_mqa_logits_decode,
+    topk_indices,
 )

@@ -23,7 +23,8 @@ MQA_ERR_UNSUPPORTED = -2
 MQA_ERR_LAUNCH = -3
 MQA_ERR_DEVICE = -4
 
-EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode", "mqa_last_error")
+EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode",
+            "mqa_topk_indices", "mqa_last_error")
 
 
 class MQAError(RuntimeError):
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH):
     lib.mqa_logits_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.paged_mqa_logits_decode.restype = I
     lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P]
+    lib.mqa_topk_indices.restype = I
+    lib.mqa_topk_indices.argtypes = [P, I, I, I, P, P]
     _lib = lib
     return lib
 
@@ -165,3 +168,21 @@ def paged_mqa_logits_decode(q_fp8: torch.Tensor, kv_cache: torch.Tensor, weights
         int(bool(clean_logits)), _tun(tunables), _stream(stream, q.device))
     _check(rc)
     return logits
+
+
+def topk_indices(logits: torch.Tensor, k: int, indices: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """logits [rows, cols] f32 -> indices [rows, k] int32: columns by decreasing
+    value (ties: smaller column first), -inf/NaN never listed, -1 padding."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, cols]")
+    rows, cols = logits.shape
+    if indices is None:
+        indices = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    if indices.shape != (rows, k):
+        raise ValueError("indices must be [rows, k]")
+    rc = load_library().mqa_topk_indices(
+        _dev(logits, "logits", torch.float32), rows, cols, int(k),
+        _dev(indices, "indices", torch.int32), _stream(stream, logits.device))
+    _check(rc)
+    return indices

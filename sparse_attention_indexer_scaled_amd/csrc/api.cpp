@@ -259,3 +259,32 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
         return fail(MQA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
 }
+
+extern "C" int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *indices,
+                                hipStream_t stream)
+{
+    if (rows < 0 || cols < 0)
+        return fail(MQA_ERR_INVALID_ARG, "rows=%d, cols=%d must be >= 0", rows, cols);
+    if (k < 1 || k > mqa::kMaxTopK)
+        return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
+    if (rows == 0)
+        return ok();
+    if (!indices || (cols > 0 && !logits))
+        return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(logits, 4) || !aligned(indices, 4))
+        return fail(MQA_ERR_INVALID_ARG, "logits and indices must be 4-byte aligned");
+    if (int rc = check_device())
+        return rc;
+    mqa::TopkLaunch p;
+    p.logits = logits;
+    p.indices = indices;
+    p.rows = rows;
+    p.cols = cols;
+    p.k = k;
+    if (trace_on())
+        std::fprintf(stderr, "[mqa] topk rows=%d cols=%d k=%d\n", rows, cols, k);
+    hipError_t e = mqa::launch_topk(p, stream);
+    if (e != hipSuccess)
+        return fail(MQA_ERR_LAUNCH, "topk launch failed: %s", hipGetErrorString(e));
+    return ok();
+}

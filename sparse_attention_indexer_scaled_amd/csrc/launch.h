@@ -41,10 +41,22 @@ struct DecodeLaunch {
     int depth;     // cache blocks in each workgroup's LDS ring, 2..7 (at most 64 KiB)
 };
 
+// Largest k of the row-wise top-k.
+constexpr int kMaxTopK = 2048;
+
+struct TopkLaunch {
+    const float *logits;
+    int32_t *indices;
+    int rows;
+    int cols;
+    int k;  // 1..kMaxTopK
+};
+
 // Bytes of LDS a decode workgroup uses for a ring of `depth` blocks.
 int decode_ring_bytes(int depth);
 
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
+hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream);
 
 } // namespace mqa

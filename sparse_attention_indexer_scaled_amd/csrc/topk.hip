@@ -1,0 +1,841 @@
+// Row-wise top-k over indexer logits (gfx950).
+//
+// The consumer of the indexer is a top-k over each logits row (index_topk of
+// 2048 or 512 on the pages: aiter PR 5047 page, "Integration" and the
+// end-to-end serving notes; the issue page about next_n tiling, "Setup").  The
+// pages do not define the selection, so this kernel implements one total
+// order: entries are ranked by value, larger first, equal values by smaller
+// column first; -inf and NaN entries (positions outside a row's window) are
+// never selected; -0.0 ranks equal to +0.0.  Row r's output is the first
+// min(k, #selectable) columns of that order, then -1.
+//
+// One workgroup (16 waves) per row.  Values map to 32-bit keys whose unsigned
+// order is the value order (key 0 = not selectable); an entry is the key in
+// the high word and ~column in the low word, so entry order is the output
+// order.  Every path ends with at most kSortCap entries in LDS that contain
+// the row's top k, and a sort of them: a bucket sort over the key range
+// (linear work) unless some bucket is crowded, else a bitonic sort.
+//
+//  1. Rows of at most kSortCap columns: gather every listable entry.
+//  2. Longer rows: a threshold from a sample of kSample entries (256 runs of
+//     16 adjacent columns), aimed at ~1.25 k survivors; one pass keeps every
+//     entry at or above it.  If between k and kSortCap entries survive, they
+//     hold the top k.
+//  3. Otherwise an exact radix select over the key bits (12 + 12 + 8): each
+//     pass histograms, in LDS, the keys that still share the threshold
+//     prefix, until the bucket holding the k-th key has at most kCand
+//     entries; then every key at or above that bucket is gathered.  A bucket
+//     that is still larger after all 32 bits is one repeated key: its first
+//     columns are taken in column order by a block-wide ordered compaction.
+//
+// Row reads are 16-byte loads, kUnroll per thread in flight: one workgroup
+// streams a whole row, so the bytes in flight per CU set its read rate.
+#include "launch.h"
+
+#include <atomic>
+
+namespace mqa {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxBins = 4096;              // 12-bit digits
+constexpr int kSortCap = 8192;              // entries gathered into LDS and sorted
+constexpr int kCand = kSortCap - kMaxTopK;  // largest bucket gathered (keys above it < k)
+constexpr int kSample = 4096;               // entries sampled for the threshold
+constexpr int kBucketMax = 32;              // largest bucket sorted in registers
+constexpr uint32_t kPosInfKey = 0xff800000u;  // order key of +inf
+constexpr int kCrowdMax = 2 * kThreads;     // largest bucket ranked by the whole block
+constexpr int kMaxCrowd = kSortCap / (kBucketMax + 1) + 1;  // crowded buckets at most
+constexpr int kUnroll = 8;                  // 16-byte loads in flight per thread
+
+static_assert(kSample == 4 * kThreads, "the sample is four entries per thread");
+static_assert(kSortCap <= 16 * kThreads, "the sort holds every gathered entry");
+
+// Unsigned order == float order; 0 for -inf and NaN; -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t order_key(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if (!(v == v) || v == -__builtin_inff())
+        return 0u;
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key on keys >= 0x00800000 (the key of -FLT_MAX): for such
+// a key t and any float v, order_key(v) >= t exactly when v >= key_value(t).
+__device__ __forceinline__ float key_value(uint32_t t)
+{
+    return __uint_as_float((t & 0x80000000u) ? (t & 0x7fffffffu) : ~t);
+}
+
+// Sort entry: key in the high word, ~column in the low word, so that a larger
+// entry ranks first (larger key, then smaller column).  0 is padding.
+__device__ __forceinline__ uint64_t entry(uint32_t key, int col)
+{
+    return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)col);
+}
+
+struct TopkShared {
+    uint32_t hist[kMaxBins];
+    uint64_t buf[kSortCap];
+    uint64_t sorted[kSortCap];  // bucket sort output
+    int count;                  // entries appended to buf (including any past its capacity)
+    int wave_total[kWaves];
+    int bcast[4];
+    uint32_t kmin, kmax, maxb;
+    int ncrowd;                     // buckets of kBucketMax < m <= kCrowdMax entries
+    int crowd_start[kMaxCrowd];
+    int crowd_m[kMaxCrowd];
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
+// Wave 0 finds the digit b such that  above + #(digits > b) < k <= above +
+// #(digits >= b),  scanning nbins digits from the top: lane l first sums
+// digits [nbins - (l+1) w, nbins - l w) with w = nbins / 64, a scan finds the
+// lane whose span holds b, and the wave then scans that span one digit per
+// lane.  Writes b, the new `above` and the bucket size to sh.bcast[0..2] (not
+// written when above + total < k), and the total to bcast[3].
+__device__ void find_threshold(TopkShared &sh, int nbins, int above, int k, int lane)
+{
+    const int w = nbins / 64;
+    const int hi = nbins - lane * w;  // exclusive upper digit of this lane's span
+    int mine = 0;
+    for (int d = hi - w; d < hi; ++d)
+        mine += (int)sh.hist[d];
+    const int incl = wave_inclusive_scan(mine, lane);
+    const int excl = incl - mine;
+    if (lane == 63)
+        sh.bcast[3] = incl;
+    const uint64_t hit = __ballot(above + excl < k && above + incl >= k);
+    if (hit == 0ull)
+        return;
+    const int span = __ffsll((unsigned long long)hit) - 1;
+    const int base = above + __shfl(excl, span, 64);
+    const int d = nbins - span * w - 1 - lane;  // lane j looks at the j-th digit from the top
+    const int c = lane < w ? (int)sh.hist[d] : 0;
+    const int run = base + wave_inclusive_scan(c, lane);  // keys with digit >= d
+    const uint64_t reach = __ballot(lane < w && run >= k);
+    if (lane == __ffsll((unsigned long long)reach) - 1) {
+        sh.bcast[0] = d;
+        sh.bcast[1] = run - c;
+        sh.bcast[2] = c;
+    }
+}
+
+// v from lane (lane ^ M) of the wave: DPP quad permutes for M = 1 and 2,
+// ds_swizzle (bit-mask mode, no LDS access) for 4..16, v_permlane32_swap for
+// 32.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane)
+{
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false);
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false);
+    } else if constexpr (M <= 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1f | (M << 10));
+    } else {
+        static_assert(M == 32, "lane exchange distance");
+        // new a = (a_lo, b_lo), new b = (a_hi, b_hi) with a = b = v
+        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return lane < 32 ? r[1] : r[0];
+    }
+}
+
+__device__ __forceinline__ uint64_t keep_side(uint64_t mine, uint64_t other, int e, int stride,
+                                              int size)
+{
+    const bool want_max = ((e & stride) == 0) == ((e & size) == 0);
+    return want_max ? (mine > other ? mine : other) : (mine < other ? mine : other);
+}
+
+constexpr int E = 16;  // entries each sorting thread holds
+
+// Compare-exchange of a pair: after it, a >= b when desc, else a <= b.
+// Selects, not a branch, so lanes never diverge.
+__device__ __forceinline__ void cmpx(uint64_t &a, uint64_t &b, bool desc)
+{
+    const bool swap = (a < b) == desc;
+    const uint64_t x = a, y = b;
+    a = swap ? y : x;
+    b = swap ? x : y;
+}
+
+// Compare-exchange at distance S < E: both entries are in this thread.
+template <int S>
+__device__ __forceinline__ void stage_thread(uint64_t (&v)[E], int tid, int size)
+{
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        if (r & S)
+            continue;
+        cmpx(v[r], v[r + S], ((E * tid + r) & size) == 0);
+    }
+}
+
+// Compare-exchange at distance M E: the partner is lane ^ M of this wave.
+template <int M>
+__device__ __forceinline__ void stage_lanes(uint64_t (&v)[E], int tid, int size, int lane)
+{
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const uint32_t lo = xor_lane<M>((uint32_t)v[r], lane);
+        const uint32_t hi = xor_lane<M>((uint32_t)(v[r] >> 32), lane);
+        v[r] = keep_side(v[r], ((uint64_t)hi << 32) | lo, E * tid + r, M * E, size);
+    }
+}
+
+// Bitonic sort of sh.buf[0, n2) into descending order (n2 a power of two, at
+// most kSortCap; entries past n2 up to the next multiple of 64 E are sorted
+// alongside and must hold padding).  The first max(n2 / E, 64) threads hold E
+// consecutive entries each in registers: partners at distance < E are in the
+// same thread, up to 32 E in the same wave (lane exchanges), and further ones
+// go through LDS.
+__device__ void sort_desc(TopkShared &sh, int n2, int tid, int lane)
+{
+    const bool act = tid < max(n2 / E, 64);  // whole waves
+    uint64_t v[E];
+    if (act) {
+#pragma unroll
+        for (int r = 0; r < E; ++r)
+            v[r] = sh.buf[E * tid + r];
+    }
+    for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 64 * E) {
+                __syncthreads();
+                if (act) {
+#pragma unroll
+                    for (int r = 0; r < E; ++r)
+                        sh.buf[E * tid + r] = v[r];
+                }
+                __syncthreads();
+                if (act) {
+#pragma unroll
+                    for (int r = 0; r < E; ++r) {
+                        const int e = E * tid + r;
+                        v[r] = keep_side(v[r], sh.buf[e ^ stride], e, stride, size);
+                    }
+                }
+                continue;
+            }
+            if (!act)
+                continue;
+            switch (stride) {
+            case 1: stage_thread<1>(v, tid, size); break;
+            case 2: stage_thread<2>(v, tid, size); break;
+            case 4: stage_thread<4>(v, tid, size); break;
+            case 8: stage_thread<8>(v, tid, size); break;
+            case E: stage_lanes<1>(v, tid, size, lane); break;
+            case 2 * E: stage_lanes<2>(v, tid, size, lane); break;
+            case 4 * E: stage_lanes<4>(v, tid, size, lane); break;
+            case 8 * E: stage_lanes<8>(v, tid, size, lane); break;
+            case 16 * E: stage_lanes<16>(v, tid, size, lane); break;
+            default: stage_lanes<32>(v, tid, size, lane); break;
+            }
+        }
+    }
+    __syncthreads();
+    if (act) {
+#pragma unroll
+        for (int r = 0; r < E; ++r)
+            sh.buf[E * tid + r] = v[r];
+    }
+    __syncthreads();
+}
+
+// Sorting networks for small buckets: descending bitonic sort of N registers.
+template <int N>
+__device__ __forceinline__ void sort_small(uint64_t (&r)[N])
+{
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                if (i & stride)
+                    continue;
+                cmpx(r[i], r[i + stride], (i & size) == 0);
+            }
+}
+
+// Sort sh.sorted[start, start + m) descending, m <= N.
+template <int N>
+__device__ __forceinline__ void sort_bucket(TopkShared &sh, int start, int m)
+{
+    uint64_t r[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        r[j] = j < m ? sh.sorted[start + j] : 0ull;
+    sort_small<N>(r);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        if (j < m)
+            sh.sorted[start + j] = r[j];
+}
+
+
+// Bucket sort of sh.buf[0, n) into sh.sorted[0, n), descending.  Keys are
+// spread over kMaxBins buckets by (key - min key) >> shift, bucket 0 holding
+// the largest keys; a prefix sum places the buckets and every thread sorts
+// four buckets of up to kBucketMax entries in registers.  Larger buckets
+// (equal logits, such as the exact zeros of tokens whose head scores are all
+// negative) are ranked by the whole block, one bucket at a time: an entry's
+// place is the number of bucket entries above it (entries are distinct, as
+// their columns are).  Linear work for spread-out keys, where a bitonic sort
+// is n log^2 n.  Returns false, with nothing written, when some bucket holds
+// more than kCrowdMax entries; the caller then sorts sh.buf itself.
+__device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int lane, int wave)
+{
+    if (tid == 0) {
+        sh.kmin = 0xffffffffu;
+        sh.kmax = 0u;
+        sh.maxb = 0u;
+        sh.ncrowd = 0;
+    }
+    for (int i = tid; i < kMaxBins; i += kThreads)
+        sh.hist[i] = 0;
+    __syncthreads();
+    // key range over the finite values (+inf, key 0xff800000, goes to the
+    // top bucket by itself)
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int i = tid; i < n; i += kThreads) {
+        const uint32_t key = (uint32_t)(sh.buf[i] >> 32);
+        lo = min(lo, key);
+        if (key != kPosInfKey)
+            hi = max(hi, key);
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
+    }
+    if (lane == 0) {
+        atomicMin(&sh.kmin, lo);
+        atomicMax(&sh.kmax, hi);
+    }
+    __syncthreads();
+    // Buckets are linear in the value, not in the key: keys are log-spaced,
+    // so a key-linear map would crowd everything into few buckets whenever
+    // the range also holds values near zero.  Double arithmetic: no overflow,
+    // and the map stays monotone (correctly rounded subtraction and product).
+    const double vmin = (double)key_value(max(sh.kmin, 0x00800000u));
+    const double vmax = sh.kmax >= sh.kmin ? (double)key_value(max(sh.kmax, 0x00800000u)) : vmin;
+    const double scale = vmax > vmin ? (double)(kMaxBins - 1) / (vmax - vmin) : 0.0;
+    auto bucket_of = [&](uint64_t e) {
+        const uint32_t key = (uint32_t)(e >> 32);
+        if (key == kPosInfKey)
+            return 0;
+        const double t = ((double)key_value(key) - vmin) * scale;
+        return kMaxBins - 1 - min((int)t, kMaxBins - 1);
+    };
+    for (int i = tid; i < n; i += kThreads)
+        atomicAdd(&sh.hist[bucket_of(sh.buf[i])], 1u);
+    __syncthreads();
+
+    // exclusive prefix sum: thread t owns buckets 4t..4t+3
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        c[j] = sh.hist[4 * tid + j];
+    const int mine = (int)(c[0] + c[1] + c[2] + c[3]);
+    const int incl = wave_inclusive_scan(mine, lane);
+    if (lane == 63)
+        sh.wave_total[wave] = incl;
+    uint32_t big = max(max(c[0], c[1]), max(c[2], c[3]));
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+        big = max(big, (uint32_t)__shfl_xor((int)big, d, 64));
+    if (lane == 0)
+        atomicMax(&sh.maxb, big);
+    __syncthreads();
+    int before = 0;
+    for (int v = 0; v < wave; ++v)
+        before += sh.wave_total[v];
+    if (sh.maxb > (uint32_t)kCrowdMax)
+        return false;  // uniform: every thread read the same maxb
+    int run = before + incl - mine;
+    int start[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        start[j] = run;
+        sh.hist[4 * tid + j] = run;  // becomes the bucket's write cursor
+        run += (int)c[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kThreads) {
+        const uint64_t e = sh.buf[i];
+        sh.sorted[atomicAdd(&sh.hist[bucket_of(e)], 1u)] = e;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = (int)c[j];
+        if (m <= 1)
+            continue;
+        if (m == 2) {
+            uint64_t a = sh.sorted[start[j]], b = sh.sorted[start[j] + 1];
+            cmpx(a, b, true);
+            sh.sorted[start[j]] = a;
+            sh.sorted[start[j] + 1] = b;
+        } else if (m <= 4) {
+            sort_bucket<4>(sh, start[j], m);
+        } else if (m <= 8) {
+            sort_bucket<8>(sh, start[j], m);
+        } else if (m <= 16) {
+            sort_bucket<16>(sh, start[j], m);
+        } else if (m <= kBucketMax) {
+            sort_bucket<kBucketMax>(sh, start[j], m);
+        } else {
+            const int slot = atomicAdd(&sh.ncrowd, 1);
+            sh.crowd_start[slot] = start[j];
+            sh.crowd_m[slot] = m;
+        }
+    }
+    __syncthreads();
+    const int ncrowd = sh.ncrowd;
+    for (int cb = 0; cb < ncrowd; ++cb) {
+        const int st = sh.crowd_start[cb], m = sh.crowd_m[cb];
+        const uint64_t e0 = tid < m ? sh.sorted[st + tid] : 0ull;
+        const uint64_t e1 = tid + kThreads < m ? sh.sorted[st + tid + kThreads] : 0ull;
+        int r0 = 0, r1 = 0;
+        int j = 0;
+        for (; j + 8 <= m; j += 8) {
+            uint64_t o[8];  // same addresses in every lane: broadcasts, eight in flight
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                o[q] = sh.sorted[st + j + q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                r0 += o[q] > e0;
+                r1 += o[q] > e1;
+            }
+        }
+        for (; j < m; ++j) {
+            const uint64_t o = sh.sorted[st + j];
+            r0 += o > e0;
+            r1 += o > e1;
+        }
+        __syncthreads();
+        if (tid < m)
+            sh.sorted[st + r0] = e0;
+        if (tid + kThreads < m)
+            sh.sorted[st + r1] = e1;
+        __syncthreads();
+    }
+    return true;
+}
+
+// Call f(v, c) for the row in groups of four columns: v holds columns
+// c..c+3; past the row end v is padded with -inf, which no caller keeps.
+// kUnroll 16-byte loads per thread are issued before any is used.
+template <typename F>
+__device__ __forceinline__ void for_each4(const float *x, int cols, int tid, F f)
+{
+    const float ninf = -__builtin_inff();
+    int i0 = 0;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        const int n4 = cols >> 2;
+        const float4 *x4 = reinterpret_cast<const float4 *>(x);
+        const float4 pad = make_float4(ninf, ninf, ninf, ninf);
+        for (int b = tid; b < n4; b += kUnroll * kThreads) {
+            float4 v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                // unconditional in-bounds load (index clamped), then select,
+                // so the compiler keeps one 16-byte load per element
+                const int i = b + u * kThreads;
+                const float4 t = x4[min(i, n4 - 1)];
+                v[u] = i < n4 ? t : pad;
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = b + u * kThreads;
+                if (i < n4)
+                    f(v[u], 4 * i);
+            }
+        }
+        i0 = 4 * n4;
+    }
+    for (int i = i0 + 4 * tid; i < cols; i += 4 * kThreads)
+        f(make_float4(x[i], i + 1 < cols ? x[i + 1] : ninf, i + 2 < cols ? x[i + 2] : ninf,
+                      i + 3 < cols ? x[i + 3] : ninf),
+          i);
+}
+
+// Append the active lanes' kept entries to sh.buf with one LDS atomic per
+// wave; every kept entry is counted in sh.count, entries past the capacity are
+// dropped (the caller checks sh.count).
+__device__ __forceinline__ void append(TopkShared &sh, bool keep, uint64_t e, int lane)
+{
+    const uint64_t active = __ballot(1);
+    const uint64_t kept = __ballot(keep);
+    if (kept == 0ull)
+        return;
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    int base = 0;
+    if (lane == leader)
+        base = atomicAdd(&sh.count, __popcll(kept));
+    base = __shfl(base, leader, 64);
+    const int pos = base + __popcll(kept & ((1ull << lane) - 1ull));
+    if (keep && pos < kSortCap)
+        sh.buf[pos] = e;
+}
+
+__device__ __forceinline__ void append4(TopkShared &sh, float4 v, int c, bool k0, bool k1, bool k2,
+                                        bool k3, int lane)
+{
+    if (__ballot(k0 || k1 || k2 || k3) == 0ull)
+        return;
+    append(sh, k0, entry(order_key(v.x), c), lane);
+    append(sh, k1, entry(order_key(v.y), c + 1), lane);
+    append(sh, k2, entry(order_key(v.z), c + 2), lane);
+    append(sh, k3, entry(order_key(v.w), c + 3), lane);
+}
+
+// First batch of the filter pass on a 16-byte aligned row (columns 4 (tid +
+// u kThreads) .. +3), loaded before the threshold is known so that its
+// latency overlaps the sampling.
+__device__ __forceinline__ void load_batch(const float *x, int cols, int b, float4 (&v)[kUnroll])
+{
+    const float ninf = -__builtin_inff();
+    const float4 pad = make_float4(ninf, ninf, ninf, ninf);
+    const int n4 = cols >> 2;
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        // unconditional in-bounds load (index clamped), then select, so the
+        // compiler keeps one 16-byte load per element
+        const int i = b + u * kThreads;
+        const float4 t = x4[min(i, n4 - 1)];
+        v[u] = i < n4 ? t : pad;
+    }
+}
+
+// Append every entry >= f0 (a finite value) to sh.buf, counting them all in
+// sh.count.  Each wave loads kUnroll 16-byte groups per thread, then takes one
+// LDS atomic for all of their survivors: lane offsets come from the ballots
+// of the four components, so no lane exchange is needed.  On an aligned row
+// `first` holds the thread's first batch (load_batch at b = tid).
+__device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, int tid, int lane,
+                            const float4 (&first)[kUnroll])
+{
+    const uint64_t lt = (1ull << lane) - 1ull;
+    auto emit = [&](const float4 (&v)[kUnroll], const int (&col)[kUnroll]) {
+        int total = 0;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            total += __popcll(__ballot(v[u].x >= f0)) + __popcll(__ballot(v[u].y >= f0)) +
+                     __popcll(__ballot(v[u].z >= f0)) + __popcll(__ballot(v[u].w >= f0));
+        if (total == 0)
+            return;
+        const uint64_t active = __ballot(1);
+        int base = 0;
+        if (lane == __ffsll((unsigned long long)active) - 1)
+            base = atomicAdd(&sh.count, total);
+        base = __builtin_amdgcn_readfirstlane(base);
+        auto put = [&](float f, int c) {
+            const uint64_t b = __ballot(f >= f0);
+            if (f >= f0 && base + __popcll(b & lt) < kSortCap)
+                sh.buf[base + __popcll(b & lt)] = entry(order_key(f), c);
+            base += __popcll(b);
+        };
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            put(v[u].x, col[u]);
+            put(v[u].y, col[u] + 1);
+            put(v[u].z, col[u] + 2);
+            put(v[u].w, col[u] + 3);
+        }
+    };
+    const float ninf = -__builtin_inff();
+    const float4 pad = make_float4(ninf, ninf, ninf, ninf);
+    float4 v[kUnroll];
+    int col[kUnroll];
+    int i0 = 0;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        const int n4 = cols >> 2;
+        for (int b = tid; b < n4; b += kUnroll * kThreads) {
+            if (b == tid) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    v[u] = first[u];
+            } else {
+                load_batch(x, cols, b, v);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                col[u] = 4 * (b + u * kThreads);
+            emit(v, col);
+        }
+        i0 = 4 * n4;
+    }
+    for (int b = i0 + 4 * tid; b < cols; b += 4 * kUnroll * kThreads) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = b + 4 * u * kThreads;
+            v[u] = pad;
+            if (i < cols)
+                v[u].x = x[i];
+            if (i + 1 < cols)
+                v[u].y = x[i + 1];
+            if (i + 2 < cols)
+                v[u].z = x[i + 2];
+            if (i + 3 < cols)
+                v[u].w = x[i + 3];
+            col[u] = i;
+        }
+        emit(v, col);
+    }
+}
+
+// A key t0 such that, judging by kSample entries of the row (256 runs of 16
+// adjacent columns, evenly spaced), about 1.25 k entries plus a few standard
+// deviations are >= t0: the 24-bit prefix of the sample's ts-th largest key,
+// located by two 12-bit histograms.  0 when the sample holds fewer than ts
+// listable keys.  Needs cols > kSample.
+__device__ uint32_t sample_threshold(TopkShared &sh, const float *x, int cols, int k, int tid,
+                                     int lane, int wave)
+{
+    const int pos = (int)(((int64_t)(tid >> 2) * cols / 256) & ~(int64_t)15) + 4 * (tid & 3);
+    float4 f;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
+        f = *reinterpret_cast<const float4 *>(x + pos);
+    else
+        f = make_float4(x[pos], x[pos + 1], x[pos + 2], x[pos + 3]);
+    const uint32_t samp[4] = {order_key(f.x), order_key(f.y), order_key(f.z), order_key(f.w)};
+    for (int i = tid; i < kMaxBins; i += kThreads)
+        sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        if (samp[s] != 0u)
+            atomicAdd(&sh.hist[samp[s] >> 20], 1u);
+    __syncthreads();
+    const float m = (float)kSample * (float)k / (float)cols;
+    const int ts = (int)ceilf(1.25f * m + 3.0f * sqrtf(m) + 4.0f);
+    if (wave == 0)
+        find_threshold(sh, kMaxBins, 0, ts, lane);
+    __syncthreads();
+    if (sh.bcast[3] < ts)
+        return 0u;
+    const uint32_t b0 = (uint32_t)sh.bcast[0];
+    const int above0 = sh.bcast[1];
+    __syncthreads();  // hist and bcast are reused below
+    for (int i = tid; i < kMaxBins; i += kThreads)
+        sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        if (samp[s] != 0u && (samp[s] >> 20) == b0)
+            atomicAdd(&sh.hist[(samp[s] >> 8) & 0xfffu], 1u);
+    __syncthreads();
+    if (wave == 0)
+        find_threshold(sh, kMaxBins, above0, ts, lane);
+    __syncthreads();
+    const uint32_t t0 = (b0 << 20) | ((uint32_t)sh.bcast[0] << 8);
+    __syncthreads();
+    return t0 > 0u ? t0 : 1u;
+}
+
+// Exact selection by radix passes (the path for any row the sampled
+// threshold does not resolve).  Leaves the entries to sort in sh.buf and
+// returns their number.
+__device__ int radix_select(TopkShared &sh, const float *x, int cols, int k, int tid, int lane,
+                            int wave)
+{
+    // The selected keys are: every key whose top `pbits` bits exceed `prefix`
+    // (there are `above` of them, fewer than k), then the largest keys of the
+    // bucket whose top bits equal `prefix`.
+    uint32_t prefix = 0;
+    int pbits = 0;
+    int above = 0;
+    int bucket = 0;
+    bool take_all = false;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int bits = pass < 2 ? 12 : 8;
+        const int nbins = 1 << bits;
+        for (int i = tid; i < nbins; i += kThreads)
+            sh.hist[i] = 0;
+        __syncthreads();
+        const int shift = 32 - pbits - bits;
+        auto count = [&](float v) {
+            const uint32_t key = order_key(v);
+            if (key != 0u && (pbits == 0 || (key >> (32 - pbits)) == prefix))
+                atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+        };
+        for_each4(x, cols, tid, [&](float4 v, int) {
+            count(v.x);
+            count(v.y);
+            count(v.z);
+            count(v.w);
+        });
+        __syncthreads();
+        if (wave == 0)
+            find_threshold(sh, nbins, above, k, lane);
+        __syncthreads();
+        if (pass == 0 && sh.bcast[3] <= k) {
+            take_all = true;  // at most k listable entries in the row
+            break;
+        }
+        prefix = (prefix << bits) | (uint32_t)sh.bcast[0];
+        pbits += bits;
+        above = sh.bcast[1];
+        bucket = sh.bcast[2];
+        __syncthreads();  // bcast is rewritten by the next pass
+        if (bucket <= kCand)
+            break;
+    }
+
+    if (tid == 0)
+        sh.count = 0;
+    __syncthreads();
+    if (take_all || bucket <= kCand) {
+        // Every listable key (take_all: at most k), or every key at or above
+        // the bucket (above + bucket < k + kCand).
+        auto keep = [&](float v) {
+            const uint32_t key = order_key(v);
+            return key != 0u && (take_all || (key >> (32 - pbits)) >= prefix);
+        };
+        for_each4(x, cols, tid, [&](float4 v, int c) {
+            append4(sh, v, c, keep(v.x), keep(v.y), keep(v.z), keep(v.w), lane);
+        });
+        __syncthreads();
+        return sh.count;
+    }
+    // pbits == 32: the bucket is one key T repeated more than kCand times.
+    // Every key above T is taken (above < k of them), then the first k - above
+    // occurrences of T in column order, by an ordered compaction over chunks.
+    const uint32_t T = prefix;
+    const int need = k - above;
+    int taken = 0;
+    for (int base = 0; base < cols; base += kThreads) {
+        const int i = base + tid;
+        const uint32_t key = i < cols ? order_key(x[i]) : 0u;
+        append(sh, key > T, entry(key, i), lane);
+        const bool tie = key == T;
+        const uint64_t ballot = __ballot(tie);
+        const int in_wave = __popcll(ballot & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            sh.wave_total[wave] = __popcll(ballot);
+        __syncthreads();
+        int before = 0, chunk = 0;
+        for (int v = 0; v < kWaves; ++v) {
+            const int c = sh.wave_total[v];
+            before += v < wave ? c : 0;
+            chunk += c;
+        }
+        const int rank = taken + before + in_wave;
+        if (tie && rank < need)
+            sh.buf[above + rank] = entry(key, i);
+        taken += chunk;
+        __syncthreads();  // wave_total is rewritten by the next chunk
+    }
+    // keys above T are at [0, above) in any order, the ties at [above, k)
+    return k;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ logits,
+                                                        int32_t *__restrict__ indices, int cols,
+                                                        int k)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
+    TopkShared &sh = *reinterpret_cast<TopkShared *>(topk_lds);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const float *x = logits + (int64_t)blockIdx.x * cols;
+    int32_t *out = indices + (int64_t)blockIdx.x * k;
+
+    if (tid == 0)
+        sh.count = 0;
+    __syncthreads();
+    int n = -1;  // entries gathered in sh.buf, once the row is resolved
+    if (cols <= kSortCap) {
+        for_each4(x, cols, tid, [&](float4 v, int c) {
+            append4(sh, v, c, order_key(v.x) != 0u, order_key(v.y) != 0u, order_key(v.z) != 0u,
+                    order_key(v.w) != 0u, lane);
+        });
+        __syncthreads();
+        n = sh.count;
+    } else {
+        float4 first[kUnroll];
+        if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
+            load_batch(x, cols, tid, first);
+        const uint32_t t0 = sample_threshold(sh, x, cols, k, tid, lane, wave);
+        if (t0 != 0u) {
+            // order_key(v) >= t0  <=>  v >= f0 (t0 raised to the smallest
+            // listable key changes nothing and keeps f0 finite, so -inf and
+            // NaN never pass)
+            const float f0 = key_value(max(t0, 0x00800000u));
+            filter_pass(sh, x, cols, f0, tid, lane, first);
+            __syncthreads();
+            const int c = sh.count;
+            if (c >= k && c <= kSortCap)
+                n = c;
+            __syncthreads();
+        }
+        if (n < 0)
+            n = radix_select(sh, x, cols, k, tid, lane, wave);
+    }
+    __syncthreads();
+
+    const uint64_t *order = sh.sorted;
+    if (!bucket_sort(sh, n, tid, lane, wave)) {
+        // Many equal or clustered keys: bitonic sort of the smallest power of
+        // two >= n, padded with 0 (ranks last).
+        int n2 = 1;
+        while (n2 < n)
+            n2 <<= 1;
+        const int span = max(n2, 64 * E);
+        for (int i = n + tid; i < span; i += kThreads)
+            sh.buf[i] = 0ull;
+        __syncthreads();
+        sort_desc(sh, n2, tid, lane);
+        order = sh.buf;
+    }
+
+    const int nsel = min(n, k);
+    for (int j = tid; j < k; j += kThreads)
+        out[j] = j < nsel ? (int32_t)(~(uint32_t)(order[j] & 0xffffffffull)) : -1;
+}
+
+} // namespace
+
+hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream)
+{
+    // The LDS block (~80 KiB) is above the default dynamic limit; raise it
+    // once per device.
+    static std::atomic<uint64_t> raised{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(raised.load() & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(TopkShared));
+        if (e != hipSuccess)
+            return e;
+        raised.fetch_or(bit);
+    }
+    hipLaunchKernelGGL(topk_kernel, dim3(p.rows), dim3(kThreads), sizeof(TopkShared), stream,
+                       p.logits, p.indices, p.cols, p.k);
+    return hipGetLastError();
+}
+
+} // namespace mqa

@@ -305,3 +305,46 @@ def make_config(idx: int, poison: bool = False):
         return make_prefill(c["M"], c["N"], seed)
     return make_decode(c["B"], c["next_n"], c["ctx"], c["mml"], seed,
                        ctx_range=c.get("ctx_range"), poison=poison)
+
+
+# Row families for the top-k over logits: shapes a logits row takes (a masked
+# window, many equal values, the special values the selection must skip or
+# rank) rather than values the op would produce; the benchmark feeds the top-k
+# real decode logits instead.
+TOPK_FAMILIES = ("normal", "small_ints", "constant", "masked_half", "specials", "narrow",
+                 "mostly_equal", "two_values", "zeros_heavy", "zeros_half")
+
+
+def topk_rows(cols: int, seed: int) -> np.ndarray:
+    """float32 [len(TOPK_FAMILIES), cols], one row per family, seeded."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((len(TOPK_FAMILIES), cols), dtype=np.float32)
+    out[0] = rng.standard_normal(cols)
+    out[1] = rng.integers(-3, 4, cols)
+    out[2] = 1.5
+    x = rng.standard_normal(cols).astype(np.float32)
+    x[rng.random(cols) < 0.5] = -np.inf
+    out[3] = x
+    x = rng.standard_normal(cols).astype(np.float32)
+    x[rng.random(cols) < 0.1] = np.nan
+    x[rng.random(cols) < 0.1] = 0.0
+    x[rng.random(cols) < 0.1] = -0.0
+    x[rng.random(cols) < 0.01] = np.inf
+    x[rng.random(cols) < 0.1] = -np.inf
+    out[4] = x
+    out[5] = rng.standard_normal(cols) * 1e-3 + 5
+    out[6] = np.where(rng.random(cols) < 0.9, np.float32(2.0),
+                      rng.standard_normal(cols).astype(np.float32))
+    x = np.full(cols, np.nextafter(np.float32(1.0), np.float32(2.0)), dtype=np.float32)
+    x[::3] = 1.0
+    out[7] = x
+    # exact zeros, as a token whose head scores are all negative produces:
+    # the k-th entry falls among many equal values
+    x = rng.standard_normal(cols).astype(np.float32)
+    x[rng.random(cols) < 0.97] = 0.0
+    out[8] = x
+    x = -np.abs(rng.standard_normal(cols)).astype(np.float32)
+    x[rng.random(cols) < 0.5] = 0.0
+    x[rng.random(cols) < 0.005] = 1.0
+    out[9] = x
+    return out

@@ -124,6 +124,19 @@ def test_decode_validation(lib):
         assert _decode(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
 
 
+def test_topk_validation(lib):
+    f = lib.mqa_topk_indices
+    assert f(None, -1, 8, 4, None, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 2, -8, 4, None, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 2, 8, 0, None, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 2, 8, 2049, None, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "k must be" in mqa.last_error()
+    assert f(None, 0, 8, 4, None, None) == 0
+    assert f(None, 2, 8, 4, None, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(P(0x1002), 2, 8, 4, P(0x2000), None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "aligned" in mqa.last_error()
+
+
 def test_binding_raises_on_missing_library(tmp_path):
     saved = _native._lib
     _native._lib = None
