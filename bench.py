@@ -373,8 +373,10 @@ def write_kernel_stats(workload_name, stats_dir, command):
              "# source_hash: %s" % source_hash(kernel_of(workload_name)),
              "name | calls | average_ns | min_ns | max_ns | percent"]
     for r in rows:
-        m = re.match(r"(.*?>)\(", r["Name"])
-        name = m.group(1) if m else r["Name"].split("(")[0]
+        # drop the argument list: the first "(" that is not part of
+        # "(anonymous namespace)"
+        full = r["Name"].replace("(anonymous namespace)", "<anon>")
+        name = full.split("(")[0].replace("<anon>", "(anonymous namespace)")
         lines.append("%s | %s | %.1f | %s | %s | %s" % (name, r["Calls"], float(r["AverageNs"]),
                                                          r["MinNs"], r["MaxNs"], r["Percentage"]))
     os.makedirs(PROFILE_DIR, exist_ok=True)
