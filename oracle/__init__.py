@@ -9,7 +9,9 @@ Python side of ``oracle/mqa_oracle.c`` (plain fp64 C, OpenMP over rows).  See
 that file for the definition, the window rules and the exactness argument.
 Inputs are numpy arrays in the op's own layouts; outputs are float64.
 
-The row-wise top-k that consumes the logits is in ``oracle.topk`` (numpy).
+The row-wise top-k that consumes the logits is in ``oracle.topk`` and the
+K-cache quantise-and-insert step that precedes decode in ``oracle.kcache``
+(both numpy).
 
 Every function here is pinned by the ``-m "not gpu"`` tests against things
 other than itself: an exact rational brute force (``oracle.brute``), numpy
