@@ -81,6 +81,9 @@ def cpu_model():
 # Top-k workloads: index -> (decode workload whose logits are ranked, k).  The
 # pages' deployments use index_topk 2048 and 512.
 TOPK_WORKLOADS = {5: (2, 2048), 6: (2, 512)}
+# K-cache insert workloads: index -> (tokens, bf16 input).  4096 tokens is the
+# long prefill chunk's K; 96 is one decode step of the MTP workload (16 x 6).
+KCACHE_WORKLOADS = {7: (4096, False), 8: (96, True)}
 
 
 class Workload:
@@ -168,9 +171,43 @@ class TopkWorkload:
         topk_indices(self.sets[i % self.nsets], self.k, indices=self.outs[i % self.nsets])
 
 
+class KcacheWorkload:
+    """K-cache quantise-and-insert of T new tokens (the step before decode)."""
+
+    def __init__(self, idx, hot):
+        import torch
+        from sparse_attention_indexer_scaled_amd import inputs
+        T, bf16 = KCACHE_WORKLOADS[idx]
+        nblocks = -(-T // 64) + 8
+        c = inputs.make_kcache_insert(T, nblocks, seed=1000 + idx, bf16=bf16, padding=0.0)
+        self.idx = idx
+        self.kind = "kcache"
+        self.cfg = {"kind": "kcache", "name": "kcache_insert_T%d_%s" % (T, "bf16" if bf16 else "fp32"),
+                    "tokens": T}
+        self.host = c
+        dtype = torch.bfloat16 if bf16 else torch.float32
+        base = dict(k=torch.from_numpy(c.k).cuda().to(dtype),
+                    slots=torch.from_numpy(c.slot_mapping).cuda(),
+                    cache=torch.from_numpy(c.kv_cache).cuda())
+        self.bytes = T * 128 * (2 if bf16 else 4) + T * 8 + T * 132
+        self.pairs = 0
+        self.flops = 0
+        set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+        nsets = 1 if hot else min(64, max(1, -(-COLD_BYTES // set_bytes)))
+        self.sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        self.nsets = nsets
+
+    def call(self, i):
+        from sparse_attention_indexer_scaled_amd import kcache_quantize_insert
+        s = self.sets[i % self.nsets]
+        kcache_quantize_insert(s["k"], s["slots"], s["cache"])
+
+
 def make_workload(idx, hot, tunables=None):
     if idx in TOPK_WORKLOADS:
         return TopkWorkload(idx, hot)
+    if idx in KCACHE_WORKLOADS:
+        return KcacheWorkload(idx, hot)
     return Workload(idx, hot, tunables)
 
 
@@ -297,6 +334,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ("device.h", "launch.h", "api.cpp", "decode.hip"),
     "prefill_kernel": ("device.h", "launch.h", "api.cpp", "prefill.hip"),
     "topk_kernel": ("launch.h", "api.cpp", "topk.hip"),
+    "kcache_insert_kernel": ("device.h", "launch.h", "api.cpp", "kcache.hip"),
 }
 
 
@@ -314,7 +352,7 @@ def source_hash(kernel):
 
 
 def kernel_of(workload_name):
-    for prefix in ("decode", "prefill", "topk"):
+    for prefix in ("decode", "prefill", "topk", "kcache_insert"):
         if workload_name.startswith(prefix):
             return prefix + "_kernel"
     raise ValueError(workload_name)
@@ -499,7 +537,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6, 7, 8) if i != args.workload]
     results, head = {}, None
     for idx in order:
         wl = make_workload(idx, args.hot, tun)
@@ -519,8 +557,10 @@ def main():
     r = results[wl.cfg["name"]]
     h = wl.host
     decode = wl.kind == "decode"
-    hbm_bound = wl.kind in ("decode", "topk")
-    if wl.kind == "topk":
+    hbm_bound = wl.kind in ("decode", "topk", "kcache")
+    if wl.kind == "kcache":
+        config = {"workload": wl.cfg["name"], "tokens": wl.cfg["tokens"], "cold": not args.hot}
+    elif wl.kind == "topk":
         config = {"workload": wl.cfg["name"], "rows": wl.cfg["rows"], "cols": wl.cfg["cols"],
                   "k": wl.k, "cold": not args.hot}
     elif decode:

@@ -174,6 +174,37 @@ int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const
 int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *indices,
                      hipStream_t stream);
 
+#define MQA_DTYPE_FP32 0
+#define MQA_DTYPE_BF16 1
+
+/*
+ * K-cache quantise-and-insert: the step that fills the paged cache read by
+ * paged_mqa_logits_decode (aiter PR 5047 page, "Motivation": K stored as fp8
+ * e4m3fn beside a per-token fp32 dequant scale; the scale is the token's
+ * absolute maximum over 448, the largest e4m3fn value).
+ *
+ *   k             [num_tokens, head_dim]  fp32 (k_dtype MQA_DTYPE_FP32) or
+ *                                         bf16 (MQA_DTYPE_BF16); finite values
+ *   slot_mapping  [num_tokens]            int64: the cache slot of each token,
+ *                                         block * kv_block_size + slot;
+ *                                         negative = padding, nothing written
+ *   kv_cache      [num_blocks] blocks in the decode layout, updated in place
+ *
+ * Per token: scale = fp32(max(amax, 1e-12) / 448) (one correctly rounded
+ * division), codes = e4m3fn(clamp(k / scale, -448, 448)) rounded to nearest,
+ * ties to even, sign kept.  The token's 128 code bytes and its scale are
+ * written to its slot; nothing else in the cache changes.  Slots at or past
+ * num_blocks * kv_block_size are skipped as well.  Two tokens mapped to the
+ * same slot race (either may win).
+ * num_tokens == 0 is a successful no-op.  Negative sizes, a bad k_dtype, NULL
+ * or misaligned pointers (k and kv_cache 16-byte, slot_mapping 8-byte) ->
+ * MQA_ERR_INVALID_ARG; head_dim != 128 or kv_block_size != 64 ->
+ * MQA_ERR_UNSUPPORTED.
+ */
+int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
+                               uint8_t *kv_cache, int num_tokens, int head_dim,
+                               int kv_block_size, int num_blocks, hipStream_t stream);
+
 /* Human-readable reason for this thread's last non-zero return ("" if none). */
 const char *mqa_last_error(void);
 

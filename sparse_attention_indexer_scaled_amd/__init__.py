@@ -16,6 +16,7 @@ from ._native import (  # noqa: F401
     MQAError,
     Tunables,
     is_supported,
+    kcache_quantize_insert,
     last_error,
     load_library,
     mqa_logits_prefill,

@@ -24,7 +24,9 @@ MQA_ERR_LAUNCH = -3
 MQA_ERR_DEVICE = -4
 
 EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode",
-            "mqa_topk_indices", "mqa_last_error")
+            "mqa_topk_indices", "mqa_kcache_quantize_insert", "mqa_last_error")
+MQA_DTYPE_FP32 = 0
+MQA_DTYPE_BF16 = 1
 
 
 class MQAError(RuntimeError):
@@ -64,6 +66,8 @@ def load_library(path: str = LIB_PATH):
     lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P]
     lib.mqa_topk_indices.restype = I
     lib.mqa_topk_indices.argtypes = [P, I, I, I, P, P]
+    lib.mqa_kcache_quantize_insert.restype = I
+    lib.mqa_kcache_quantize_insert.argtypes = [P, I, P, P, I, I, I, I, P]
     _lib = lib
     return lib
 
@@ -186,3 +190,25 @@ def topk_indices(logits: torch.Tensor, k: int, indices: Optional[torch.Tensor] =
         _dev(indices, "indices", torch.int32), _stream(stream, logits.device))
     _check(rc)
     return indices
+
+
+def kcache_quantize_insert(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+                           kv_block_size: int = 64, stream=None) -> torch.Tensor:
+    """k [T, 128] float32 or bfloat16, slot_mapping [T] int64 (negative = skip),
+    kv_cache [num_blocks, kv_block_size * 132] uint8 (updated in place)."""
+    if k.dim() != 2:
+        raise ValueError("k must be [num_tokens, head_dim]")
+    T, D = k.shape
+    dtype = {torch.float32: MQA_DTYPE_FP32, torch.bfloat16: MQA_DTYPE_BF16}.get(k.dtype)
+    if dtype is None:
+        raise TypeError("k must be float32 or bfloat16, got %s" % k.dtype)
+    cache = _bytes(kv_cache, "kv_cache")
+    if cache.dim() != 2 or cache.shape[1] != kv_block_size * (D + 4):
+        raise ValueError("kv_cache must be [num_blocks, kv_block_size*(head_dim+4)] bytes")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    rc = load_library().mqa_kcache_quantize_insert(
+        _dev(k, "k"), dtype, _dev(slot_mapping, "slot_mapping", torch.int64), _dev(cache, "kv_cache"),
+        T, D, int(kv_block_size), cache.shape[0], _stream(stream, k.device))
+    _check(rc)
+    return kv_cache

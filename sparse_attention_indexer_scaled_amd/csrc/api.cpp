@@ -288,3 +288,41 @@ extern "C" int mqa_topk_indices(const float *logits, int rows, int cols, int k, 
         return fail(MQA_ERR_LAUNCH, "topk launch failed: %s", hipGetErrorString(e));
     return ok();
 }
+
+extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
+                                          uint8_t *kv_cache, int num_tokens, int head_dim,
+                                          int kv_block_size, int num_blocks, hipStream_t stream)
+{
+    if (num_tokens < 0 || num_blocks < 0)
+        return fail(MQA_ERR_INVALID_ARG, "num_tokens=%d, num_blocks=%d must be >= 0", num_tokens,
+                    num_blocks);
+    if (k_dtype != MQA_DTYPE_FP32 && k_dtype != MQA_DTYPE_BF16)
+        return fail(MQA_ERR_INVALID_ARG, "k_dtype must be MQA_DTYPE_FP32 or MQA_DTYPE_BF16 (got %d)",
+                    k_dtype);
+    if (head_dim != 128 || kv_block_size != 64)
+        return fail(MQA_ERR_UNSUPPORTED,
+                    "K-cache insert supports head_dim=128, kv_block_size=64 (got %d, %d)", head_dim,
+                    kv_block_size);
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !slot_mapping || !kv_cache)
+        return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(k, 16) || !aligned(kv_cache, 16) || !aligned(slot_mapping, 8))
+        return fail(MQA_ERR_INVALID_ARG, "k and kv_cache must be 16-byte aligned, slot_mapping 8-byte");
+    if (int rc = check_device())
+        return rc;
+    mqa::KcacheLaunch p;
+    p.k = k;
+    p.slots = slot_mapping;
+    p.cache = kv_cache;
+    p.tokens = num_tokens;
+    p.block_size = kv_block_size;
+    p.num_slots = (int64_t)num_blocks * kv_block_size;
+    p.bf16 = k_dtype == MQA_DTYPE_BF16;
+    if (trace_on())
+        std::fprintf(stderr, "[mqa] kcache insert tokens=%d dtype=%d\n", num_tokens, k_dtype);
+    hipError_t e = mqa::launch_kcache_insert(p, stream);
+    if (e != hipSuccess)
+        return fail(MQA_ERR_LAUNCH, "kcache insert launch failed: %s", hipGetErrorString(e));
+    return ok();
+}

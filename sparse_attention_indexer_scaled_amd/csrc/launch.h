@@ -52,11 +52,22 @@ struct TopkLaunch {
     int k;  // 1..kMaxTopK
 };
 
+struct KcacheLaunch {
+    const void *k;        // [tokens, 128] fp32 or bf16
+    const int64_t *slots; // [tokens]
+    uint8_t *cache;       // [num_slots / block_size] blocks of block_size * 132 bytes
+    int tokens;
+    int block_size;
+    int64_t num_slots;    // num_blocks * block_size
+    int bf16;
+};
+
 // Bytes of LDS a decode workgroup uses for a ring of `depth` blocks.
 int decode_ring_bytes(int depth);
 
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream);
+hipError_t launch_kcache_insert(const KcacheLaunch &p, hipStream_t stream);
 
 } // namespace mqa

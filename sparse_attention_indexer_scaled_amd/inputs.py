@@ -348,3 +348,34 @@ def topk_rows(cols: int, seed: int) -> np.ndarray:
     x[rng.random(cols) < 0.005] = 1.0
     out[9] = x
     return out
+
+
+@dataclasses.dataclass
+class KcacheInsertInputs:
+    k: np.ndarray             # [T, D] float32 (bf16-representable when bf16=True)
+    slot_mapping: np.ndarray  # [T] int64, distinct slots, -1 = padding
+    kv_cache: np.ndarray      # [num_blocks, block_size * (D + 4)] uint8, prior contents
+    block_size: int
+    bf16: bool
+
+
+def make_kcache_insert(T: int, num_blocks: int, seed: int, block_size: int = KV_BLOCK,
+                       D: int = HEAD_DIM, bf16: bool = False, padding: float = 0.1):
+    """New K rows for the cache: N(0,1) rows with per-row magnitudes spread
+    over 1e-3..1e3 (so scales span many binades), each mapped to a distinct
+    random slot of a cache holding random prior bytes; a fraction `padding`
+    of the tokens is padding (slot -1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = rng.standard_normal((T, D)).astype(np.float32)
+    k *= (10.0 ** rng.uniform(-3, 3, (T, 1))).astype(np.float32)
+    if T:
+        k[0] = 0.0  # an all-zero token: the scale floor
+    if bf16:
+        k = (torch.from_numpy(k).to(torch.bfloat16).to(torch.float32)).numpy()
+    nslots = num_blocks * block_size
+    if T > nslots:
+        raise ValueError("more tokens than cache slots")
+    slots = rng.permutation(nslots)[:T].astype(np.int64)
+    slots[rng.random(T) < padding] = -1
+    cache = rng.integers(0, 256, (num_blocks, block_size * (D + 4)), dtype=np.uint8)
+    return KcacheInsertInputs(k, slots, cache, block_size, bf16)

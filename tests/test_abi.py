@@ -137,6 +137,20 @@ def test_topk_validation(lib):
     assert "aligned" in mqa.last_error()
 
 
+def test_kcache_validation(lib):
+    f = lib.mqa_kcache_quantize_insert
+    assert f(None, 0, None, None, -1, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 2, None, None, 5, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "k_dtype" in mqa.last_error()
+    assert f(None, 0, None, None, 5, 64, 64, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 1, None, None, 5, 128, 16, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 0, 128, 64, 4, None) == 0
+    assert f(None, 0, None, None, 5, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(P(0x1004), 0, P(0x2000), P(0x3000), 5, 128, 64, 4, None) == \
+        mqa._native.MQA_ERR_INVALID_ARG
+    assert "aligned" in mqa.last_error()
+
+
 def test_binding_raises_on_missing_library(tmp_path):
     saved = _native._lib
     _native._lib = None
