@@ -112,7 +112,8 @@ class Workload:
                         ctx=dev(host.context_lens), bt=dev(host.block_tables))
             self.out_shape = (host.B * host.next_n, host.max_model_len)
             self.bytes = workload.decode_essential_bytes(host.B, host.next_n, host.context_lens,
-                                                         host.max_model_len)
+                                                         host.max_model_len,
+                                                         block_size=host.block_size)
             self.pairs = workload.decode_valid_pairs(host.next_n, host.context_lens,
                                                      host.max_model_len)
             set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
@@ -134,7 +135,8 @@ class Workload:
                                tunables=self.tun)
         else:
             paged_mqa_logits_decode(s["q"], s["cache"], s["w"], s["ctx"], s["bt"],
-                                    self.host.max_model_len, logits=out, tunables=self.tun)
+                                    self.host.max_model_len, kv_block_size=self.host.block_size,
+                                    logits=out, tunables=self.tun)
 
 
 class TopkWorkload:
@@ -537,7 +539,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 7, 8) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10) if i != args.workload]
     results, head = {}, None
     for idx in order:
         wl = make_workload(idx, args.hot, tun)
@@ -566,7 +568,7 @@ def main():
     elif decode:
         config = {"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
                   "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
-                  "heads": 32, "head_dim": 128, "kv_block_size": 64, "cold": not args.hot}
+                  "heads": 32, "head_dim": 128, "kv_block_size": h.block_size, "cold": not args.hot}
     else:
         config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": 32, "head_dim": 128,
                   "cold": not args.hot}

@@ -79,8 +79,8 @@ typedef struct mqa_tunables {
 /*
  * Support gate (both pages, "Technical Details": the kernels are fixed to 32
  * heads and head_dim 128 on gfx950, and callers route other shapes elsewhere
- * instead of failing).  kv_block_size: 0 asks about prefill, 64 about paged
- * decode with 64-token blocks.  Returns 1 if the current HIP device is gfx950
+ * instead of failing).  kv_block_size: 0 asks about prefill, 1, 16, 64 or
+ * 128 about paged decode with blocks of that many tokens.  Returns 1 if the current HIP device is gfx950
  * and the shape is supported, else 0.  Never fails.
  */
 int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
@@ -143,6 +143,8 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * Entries past that are never read.  Scales must be >= 0.  Cache slots past a
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
+ * kv_block_size 1, 16, 64 or 128 (ring_depth tunable other than 4 only with
+ * 64).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
  * negative sizes, NULL or misaligned pointers -> MQA_ERR_INVALID_ARG; a shape
  * or block size outside the gate -> MQA_ERR_UNSUPPORTED.

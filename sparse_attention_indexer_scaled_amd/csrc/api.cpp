@@ -80,7 +80,9 @@ int check_device()
 
 bool shape_supported(int num_heads, int head_dim, int kv_block_size)
 {
-    return num_heads == 32 && head_dim == 128 && (kv_block_size == 0 || kv_block_size == 64);
+    return num_heads == 32 && head_dim == 128 &&
+           (kv_block_size == 0 || kv_block_size == 1 || kv_block_size == 16 ||
+            kv_block_size == 64 || kv_block_size == 128);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -194,16 +196,18 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
         return fail(MQA_ERR_INVALID_ARG, "next_n must be in 1..8 (got %d)", next_n);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "decode supports num_heads=32, head_dim=128, kv_block_size=64 (got %d, %d, %d)",
+                    "decode supports num_heads=32, head_dim=128, kv_block_size 1, 16, 64 or 128 "
+                    "(got %d, %d, %d)",
                     num_heads, head_dim, kv_block_size);
     mqa_tunables t = {};
     if (tun)
         t = *tun;
     if (t.rows_per_block < 0 || t.rows_per_block > 4 || t.split_kv < 0 || t.num_warps != 0 ||
-        t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7)
+        t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7 ||
+        (kv_block_size != 64 && t.ring_depth != 0 && t.ring_depth != 4))
         return fail(MQA_ERR_INVALID_ARG,
-                    "decode tunables: rows_per_block in 0..4, split_kv >= 0, ring_depth 0 or 2..7, "
-                    "num_warps 0");
+                    "decode tunables: rows_per_block in 0..4, split_kv >= 0, ring_depth 0 or 2..7 "
+                    "(0 or 4 unless kv_block_size is 64), num_warps 0");
     if (batch == 0 || max_model_len == 0)
         return ok();
     if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables || !logits)
@@ -241,6 +245,7 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     rows = std::min(rows, next_n);
     p.rows = rows;
     p.depth = t.ring_depth ? t.ring_depth : 4;
+    p.block_size = kv_block_size;
     const int64_t steps_max = ceil_div(max_model_len, 64);
     if (t.split_kv) {
         p.split_kv = t.split_kv;
@@ -299,10 +304,11 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
     if (k_dtype != MQA_DTYPE_FP32 && k_dtype != MQA_DTYPE_BF16)
         return fail(MQA_ERR_INVALID_ARG, "k_dtype must be MQA_DTYPE_FP32 or MQA_DTYPE_BF16 (got %d)",
                     k_dtype);
-    if (head_dim != 128 || kv_block_size != 64)
+    if (!shape_supported(32, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "K-cache insert supports head_dim=128, kv_block_size=64 (got %d, %d)", head_dim,
-                    kv_block_size);
+                    "K-cache insert supports head_dim=128, kv_block_size 1, 16, 64 or 128 "
+                    "(got %d, %d)",
+                    head_dim, kv_block_size);
     if (num_tokens == 0)
         return ok();
     if (!k || !slot_mapping || !kv_cache)

@@ -37,7 +37,7 @@
 namespace mqa {
 namespace {
 
-constexpr int kSlotBytes = kBlockBytes;            // one cache block per ring slot
+constexpr int kSlotBytes = kBlockBytes;  // ring slot: one 64-token step, K rows + scales
 constexpr int kChunks = kDim * kBlock / 1024 + 1;  // 8 x 1 KiB of K + 1 x 256 B of scales
 
 // Sizes and launch shape; the pointers are separate __restrict__ kernel
@@ -58,20 +58,72 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // MI355X this is worth about 10% on the long-context decode.
 constexpr int kStreamHint = 2;
 
-// Request one cache block into ring slot `slot`.  Chunk c < 8 moves tokens
-// 8c..8c+7 (1 KiB of whole 128-byte rows, so the global read is fully
-// coalesced); chunk 8 moves the 64 scales.  A global_load_lds instruction
-// writes lane i's 16 bytes at slot + 1024 c + 16 i, so the lane -> granule
-// assignment decides the LDS layout: position i of chunk c holds granule
-// q = i ^ (8 (c & 1)) of the chunk, where q = 8 u + tau is 16-byte granule u
-// of token 8c + tau.  Odd chunks swap the two 128-byte halves of each 256-byte
-// row, so that one 16-lane pass of ds_read_b128, which reads two neighbouring
-// chunks, covers all 64 LDS banks once.  Wave g of G issues K chunks g, g + G,
-// ... and the last wave also the scales, so every wave issues at least
-// kChunks / G loads per block.
-template <int G>
-__device__ __forceinline__ void request_block(lds_u8 *slot, const uint8_t *blk, int g, int lane)
+// Where the 64 tokens of one step come from in a cache of BS-token blocks,
+// and how they are requested into a ring slot.  The slot layout is the same
+// for every block size (see read_block): 8 x 1 KiB chunks of K rows, then the
+// 64 scales.  A global_load_lds instruction writes lane i's 16 bytes at
+// slot + 1024 c + 16 i, so the lane -> granule assignment decides the LDS
+// layout: position i of chunk c holds granule q = i ^ (8 (c & 1)) of the
+// chunk, where q = 8 u + tau is 16-byte granule u of token 8c + tau.  Odd
+// chunks swap the two 128-byte halves of each 256-byte row, so that one
+// 16-lane pass of ds_read_b128, which reads two neighbouring chunks, covers
+// all 64 LDS banks once.  Wave g of G issues K chunks g, g + G, ... and the
+// last wave also the scales, so every wave issues at least kChunks / G loads
+// per step.
+//
+// Blocks of 16 or more tokens hold whole 8-token chunks, so each chunk is one
+// coalesced 1 KiB read; the step's table entries (64 / BS of them, or one
+// entry covering several steps) are read with scalar loads.
+// The block pointers of one step (one per table entry the step touches).
+template <int N>
+struct StepBlocks {
+    const uint8_t *p[N];
+};
+
+constexpr int entries_per_step(int bs) { return bs >= kStep ? 1 : kStep / bs; }
+
+template <int BS>
+struct Gather {
+    static_assert(BS == 16 || BS == 64 || BS == 128, "block sizes with whole chunks");
+    static constexpr int kEntries = entries_per_step(BS);        // table entries per step
+    static constexpr int64_t kBytes = (int64_t)BS * (kDim + 4);  // bytes per block
+
+    struct Src {
+        StepBlocks<kEntries> blk;
+        int off;  // first token of the step within its block (BS > 64)
+    };
+
+    // last: index of the sequence's last table entry that holds a token of
+    // the window.  Entries past it are never read (they may be padding): a
+    // step that ends beyond the context reuses the last entry, whose data
+    // never reaches an output.
+    __device__ static __forceinline__ Src fetch(const uint8_t *cache, const int32_t *table, int st,
+                                                int last)
+    {
+        Src src;
+        if (BS >= kStep) {
+            const int tok = st * kStep;
+            src.blk.p[0] = cache + (int64_t)table[tok / BS] * kBytes;
+            src.off = tok % BS;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kEntries; ++e)
+                src.blk.p[e] = cache + (int64_t)table[min(st * kEntries + e, last)] * kBytes;
+            src.off = 0;
+        }
+        return src;
+    }
+
+};
+
+// Request a step into ring slot `slot` (wave g of G; see Gather): blk_of and
+// off are the fields of the step's Gather<BS>::Src (passed by value, so the
+// pointers stay in registers).
+template <int G, int BS>
+__device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_per_step(BS)> blk_of,
+                                             int off, int g, int lane)
 {
+    constexpr int kEntries = entries_per_step(BS);
     constexpr int KC = kChunks - 1;
     constexpr int J = (KC + G - 1) / G;
 #pragma unroll
@@ -79,13 +131,102 @@ __device__ __forceinline__ void request_block(lds_u8 *slot, const uint8_t *blk, 
         const int c = g + G * j;
         if (G * J == KC || c < KC) {
             const int q = lane ^ (8 * (c & 1));
-            __builtin_amdgcn_global_load_lds(blk + (8 * c + (q & 7)) * kDim + (q >> 3) * 16,
+            const int e = BS >= kStep ? 0 : (8 * c) / BS;  // wave-uniform
+            const uint8_t *blk = blk_of.p[0];
+#pragma unroll
+            for (int i = 1; i < kEntries; ++i)  // selects, not a dynamic index
+                if (e == i)
+                    blk = blk_of.p[i];
+            const int row = (BS >= kStep ? off + 8 * c : (8 * c) % BS) + (q & 7);
+            __builtin_amdgcn_global_load_lds(blk + row * kDim + (q >> 3) * 16,
                                              slot + 1024 * c, 16, 0, kStreamHint);
         }
     }
-    if (G == 1 || g == G - 1)
-        __builtin_amdgcn_global_load_lds(blk + kBlock * kDim + lane * 4, slot + kBlock * kDim, 4, 0,
+    if (G == 1 || g == G - 1) {
+        const uint8_t *blk = blk_of.p[0];
+        int row = off + lane;
+        if (BS < kStep) {
+#pragma unroll
+            for (int e = 1; e < kEntries; ++e)
+                if (lane >= e * BS)
+                    blk = blk_of.p[e];
+            row = lane % BS;
+        }
+        __builtin_amdgcn_global_load_lds(blk + BS * kDim + row * 4, slot + kBlock * kDim, 4, 0,
                                          kStreamHint);
+    }
+}
+
+// Per-token blocks (BS = 1, the plain co-packed layout): token p's 128 K
+// bytes and 4 scale bytes sit at 132 * table[p], so rows are only 4-byte
+// aligned and every token has its own table entry.  A step's 64 entries are
+// staged in LDS (one global->LDS dword load, by wave 0, well ahead: see the
+// kernel), each wave reads the entries its loads need, and K moves with
+// 4-byte global->LDS loads: dword load jj of chunk c writes LDS bytes
+// 1024 c + 256 jj + 4 i from lane i, i.e. byte 4 (i % 4) of granule
+// position 16 jj + i / 4, which holds granule q = position ^ 8 (c & 1): token
+// 8c + (i / 4) % 8, 16-byte granule 2 jj + ((i / 32) ^ (c & 1)).  So each lane
+// needs one entry per chunk, and four loads move a chunk.
+constexpr int kTokLoadsPerChunk = 4;
+
+__device__ __forceinline__ int32_t lds_read_i32(uint32_t addr)
+{
+    int32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, const uint8_t *cache,
+                                               int g, int lane)
+{
+    constexpr int KC = kChunks - 1;
+    constexpr int J = (KC + G - 1) / G;
+    const bool scales = G == 1 || g == G - 1;
+    int32_t ent[J];
+    int32_t ent_s = 0;
+    // Inline asm reads, completed by an explicit wait: the compiler would
+    // otherwise make them wait for every outstanding global->LDS load.
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = g + G * j;
+        ent[j] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * (8 * c + ((lane >> 2) & 7))) : 0;
+    }
+    if (scales)
+        ent_s = lds_read_i32(entries + 4 * lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        asm volatile("" : "+v"(ent[j]));
+        const int c = g + G * j;
+        if (G * J == KC || c < KC) {
+            const uint8_t *src = cache + (int64_t)ent[j] * (kDim + 4) +
+                                 16 * (((lane >> 5) ^ (c & 1))) + 4 * (lane & 3);
+#pragma unroll
+            for (int jj = 0; jj < kTokLoadsPerChunk; ++jj)
+                __builtin_amdgcn_global_load_lds(src + 32 * jj, slot + 1024 * c + 256 * jj, 4, 0,
+                                                 kStreamHint);
+        }
+    }
+    if (scales) {
+        asm volatile("" : "+v"(ent_s));
+        __builtin_amdgcn_global_load_lds(cache + (int64_t)ent_s * (kDim + 4) + kDim,
+                                         slot + kBlock * kDim, 4, 0, kStreamHint);
+    }
+}
+
+// The fewest global->LDS loads any wave of G issues per step, with
+// loads_per_chunk loads per K chunk and the scale load on the last wave.
+constexpr int min_loads_per_step(int G, int loads_per_chunk)
+{
+    int m = 1 << 30;
+    for (int g = 0; g < G; ++g) {
+        int n = g == G - 1 ? 1 : 0;
+        for (int c = g; c < kChunks - 1; c += G)
+            n += loads_per_chunk;
+        m = n < m ? n : m;
+    }
+    return m;
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding.
@@ -173,7 +314,7 @@ __device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[R],
     }
 }
 
-template <int R, int G, int D>
+template <int R, int G, int D, int BS>
 __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restrict__ qbuf,
                                                         const uint8_t *__restrict__ cache,
                                                         const float *__restrict__ wbuf,
@@ -257,25 +398,61 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         const int32_t *table = tables + (int64_t)b * a.mbps;
         lds_u8 *ring = (lds_u8 *)ring_mem;
         const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+        using Gth = Gather<(BS == 1 ? kBlock : BS)>;  // unused for BS = 1
+        const int last_entry = (nvalid - 1) / BS;
+        // BS = 1: table ring of 2D - 2 steps of 64 entries after the K ring.
+        // Entries for step y are loaded (by wave 0) in the iteration that
+        // requests K for step y - D + 1, before that request, and read in the
+        // iteration that requests step y: by then the wait for step
+        // y - D + 1 has covered them, and the barrier published them.
+        constexpr int kTabSlots = 2 * D - 2;
+        lds_u8 *tring = ring + D * kSlotBytes;
+        const uint32_t tring_addr = ring_addr + D * kSlotBytes;
+        auto request_table = [&](int y) {  // wave 0 only
+            const int tok = min(y * kStep + lane, last_entry);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(table + tok),
+                                             tring + ((y - st0) % kTabSlots) * (kStep * 4), 4, 0, 0);
+        };
         // Fill D-1 slots (fewer when the split has fewer steps).
+        if constexpr (BS == 1) {
+            if (g == 0) {
 #pragma unroll
-        for (int i = 0; i < D - 1; ++i)
-            if (st0 + i < st1)
-                request_block<G>(ring + i * kSlotBytes, cache + (int64_t)table[st0 + i] * kBlockBytes,
-                                 g, lane);
+                for (int i = 0; i < kTabSlots; ++i)
+                    if (st0 + i < st1)
+                        request_table(st0 + i);
+            }
+            wait_vm<0>();
+            __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int i = 0; i < D - 1; ++i)
+                if (st0 + i < st1)
+                    request_tokens<G>(ring + i * kSlotBytes, tring_addr + i * (kStep * 4), cache, g,
+                                      lane);
+        } else {
+#pragma unroll
+            for (int i = 0; i < D - 1; ++i)
+                if (st0 + i < st1) {
+                    const typename Gth::Src src = Gth::fetch(cache, table, st0 + i, last_entry);
+                    request_step<G, BS>(ring + i * kSlotBytes, src.blk, src.off, g, lane);
+                }
+        }
         // Between requesting block k and waiting for it a wave requests the
-        // D - 2 following blocks, at least kChunks / G loads each, so waiting
-        // until at most that many loads are outstanding guarantees block k
-        // (loads complete in order; stores counted as well only make the wait
-        // stricter).  In the last D - 2 steps fewer blocks follow and the wave
-        // waits for everything.
-        constexpr int kWait = (D - 2) * (kChunks / G);
+        // D - 2 following blocks, at least min_loads_per_step loads each, so
+        // waiting until at most that many loads are outstanding guarantees
+        // block k (loads complete in order; stores and table loads counted as
+        // well only make the wait stricter).  In the last D - 2 steps fewer
+        // blocks follow and the wave waits for everything.
+        // (vmcnt holds at most 63; a smaller count is a stricter wait)
+        constexpr int kWaitRaw = (D - 2) * min_loads_per_step(G, BS == 1 ? kTokLoadsPerChunk : 1);
+        constexpr int kWait = kWaitRaw < 63 ? kWaitRaw : 63;
         int rd = 0;      // slot of step st
         int wr = D - 1;  // slot of step st + D - 1
         // Block-table entries are read one step ahead: a scalar load is only
         // waited for together with every outstanding LDS read, so its result
         // must not be needed between read_block and read_wait.
-        int32_t next_blk = table[min(st0 + D - 1, st1 - 1)];
+        typename Gth::Src next{};
+        if constexpr (BS != 1)
+            next = Gth::fetch(cache, table, min(st0 + D - 1, st1 - 1), last_entry);
         float prev_tot[2][NP];
         for (int st = st0; st < st1; ++st) {
             // this wave's part of block st has landed ...
@@ -285,10 +462,18 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                 wait_vm<0>();
             // ... and every wave's part; nobody reads slot st-1 any more
             __builtin_amdgcn_s_barrier();
-            if (st + D - 1 < st1)
-                request_block<G>(ring + wr * kSlotBytes, cache + (int64_t)next_blk * kBlockBytes, g,
-                                 lane);
-            next_blk = table[min(st + D, st1 - 1)];
+            if constexpr (BS == 1) {
+                if (g == 0 && st + kTabSlots < st1)
+                    request_table(st + kTabSlots);
+                if (st + D - 1 < st1)
+                    request_tokens<G>(ring + wr * kSlotBytes,
+                                      tring_addr + ((st + D - 1 - st0) % kTabSlots) * (kStep * 4),
+                                      cache, g, lane);
+            } else {
+                if (st + D - 1 < st1)
+                    request_step<G, BS>(ring + wr * kSlotBytes, next.blk, next.off, g, lane);
+                next = Gth::fetch(cache, table, min(st + D, st1 - 1), last_entry);
+            }
             KStep kb;
             read_block(kb, ring_addr + rd * kSlotBytes, lane);
             if (st > st0)
@@ -310,11 +495,11 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
     }
 }
 
-template <int R, int G, int D>
-hipError_t launch_rgd(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
+template <int R, int G, int D, int BS>
+hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
-    const size_t lds = (size_t)D * kSlotBytes;
-    hipLaunchKernelGGL((decode_kernel<R, G, D>), dim3(grid), dim3(64 * G), lds, stream, p.q,
+    const size_t lds = (size_t)D * kSlotBytes + (BS == 1 ? (size_t)(2 * D - 2) * kStep * 4 : 0);
+    hipLaunchKernelGGL((decode_kernel<R, G, D, BS>), dim3(grid), dim3(64 * G), lds, stream, p.q,
                        p.cache, p.weights, p.context_lens, p.block_tables, p.logits, a);
     return hipGetLastError();
 }
@@ -322,13 +507,24 @@ hipError_t launch_rgd(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipS
 template <int R, int G>
 hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
-    switch (p.depth) {
-    case 2: return launch_rgd<R, G, 2>(p, a, grid, stream);
-    case 3: return launch_rgd<R, G, 3>(p, a, grid, stream);
-    case 4: return launch_rgd<R, G, 4>(p, a, grid, stream);
-    case 5: return launch_rgd<R, G, 5>(p, a, grid, stream);
-    case 6: return launch_rgd<R, G, 6>(p, a, grid, stream);
-    case 7: return launch_rgd<R, G, 7>(p, a, grid, stream);
+    if (p.block_size == 64) {
+        switch (p.depth) {
+        case 2: return launch_rgdb<R, G, 2, 64>(p, a, grid, stream);
+        case 3: return launch_rgdb<R, G, 3, 64>(p, a, grid, stream);
+        case 4: return launch_rgdb<R, G, 4, 64>(p, a, grid, stream);
+        case 5: return launch_rgdb<R, G, 5, 64>(p, a, grid, stream);
+        case 6: return launch_rgdb<R, G, 6, 64>(p, a, grid, stream);
+        case 7: return launch_rgdb<R, G, 7, 64>(p, a, grid, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    // other block sizes: the default ring depth only
+    if (p.depth != 4)
+        return hipErrorInvalidValue;
+    switch (p.block_size) {
+    case 1: return launch_rgdb<R, G, 4, 1>(p, a, grid, stream);
+    case 16: return launch_rgdb<R, G, 4, 16>(p, a, grid, stream);
+    case 128: return launch_rgdb<R, G, 4, 128>(p, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -38,7 +38,9 @@ struct DecodeLaunch {
     int clean;
     int rows;      // rows per wave (R), 1..4, <= next_n; ceil(next_n / R) waves per workgroup
     int split_kv;  // workgroups per sequence
-    int depth;     // cache blocks in each workgroup's LDS ring, 2..7 (at most 64 KiB)
+    int depth;     // 64-token steps in each workgroup's LDS ring, 2..7 (at most 64 KiB);
+                   // 4 for block sizes other than 64
+    int block_size;  // tokens per cache block: 1, 16, 64 or 128
 };
 
 // Largest k of the row-wise top-k.

@@ -294,17 +294,24 @@ CONFIGS = {
     3: dict(kind="prefill", name="prefill_M4096_N32768", M=4096, N=32768),
     4: dict(kind="decode", name="decode_B64_nn4_ragged1K-128K", B=64, next_n=4, ctx=None,
             ctx_range=(1024, 131072), mml=131072),
+    # the headline decode shape in the other cache layouts (16-token blocks,
+    # and per-token blocks: the plain co-packed cache)
+    9: dict(kind="decode", name="decode_B16_nn6_ctx131072_bs16", B=16, next_n=6, ctx=131072,
+            mml=131072, block_size=16),
+    10: dict(kind="decode", name="decode_B16_nn6_ctx131072_bs1", B=16, next_n=6, ctx=131072,
+             mml=131072, block_size=1),
 }
 
 
 def make_config(idx: int, poison: bool = False):
-    """The five named workloads, seed = 1000 + index."""
+    """The named workloads, seed = 1000 + index."""
     c = CONFIGS[idx]
     seed = 1000 + idx
     if c["kind"] == "prefill":
         return make_prefill(c["M"], c["N"], seed)
     return make_decode(c["B"], c["next_n"], c["ctx"], c["mml"], seed,
-                       ctx_range=c.get("ctx_range"), poison=poison)
+                       ctx_range=c.get("ctx_range"), poison=poison,
+                       block_size=c.get("block_size", KV_BLOCK))
 
 
 # Row families for the top-k over logits: shapes a logits row takes (a masked

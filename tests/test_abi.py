@@ -65,7 +65,7 @@ def test_error_codes_match_header():
 
 
 def test_gate_rejects_other_shapes(lib):
-    for h, d, bs in [(64, 128, 0), (32, 64, 0), (128, 128, 64), (32, 128, 16), (32, 128, 1)]:
+    for h, d, bs in [(64, 128, 0), (32, 64, 0), (128, 128, 64), (32, 128, 32), (32, 128, 2)]:
         assert lib.mqa_is_supported(h, d, bs) == 0
 
 
@@ -110,7 +110,8 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls, B=-1) == mqa._native.MQA_ERR_INVALID_ARG
     assert _decode(lib, nulls, nn=0) == mqa._native.MQA_ERR_INVALID_ARG
     assert _decode(lib, nulls, nn=9) == mqa._native.MQA_ERR_INVALID_ARG
-    assert _decode(lib, nulls, bs=16) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, bs=32) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, bs=16) == mqa._native.MQA_ERR_INVALID_ARG  # supported; NULLs
     assert _decode(lib, nulls, bs=0) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, H=64) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, B=0) == 0
@@ -118,6 +119,8 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls) == mqa._native.MQA_ERR_INVALID_ARG
     odd = [P(0x2002)] * 6
     assert _decode(lib, odd) == mqa._native.MQA_ERR_INVALID_ARG
+    bad = _native.Tunables(ring_depth=3)  # other depths only with 64-token blocks
+    assert _decode(lib, nulls, bs=16, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
     for bad in (_native.Tunables(rows_per_block=5), _native.Tunables(ring_depth=1),
                 _native.Tunables(ring_depth=8), _native.Tunables(num_warps=2),
                 _native.Tunables(split_kv=-1)):
@@ -143,7 +146,7 @@ def test_kcache_validation(lib):
     assert f(None, 2, None, None, 5, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert "k_dtype" in mqa.last_error()
     assert f(None, 0, None, None, 5, 64, 64, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert f(None, 1, None, None, 5, 128, 16, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 1, None, None, 5, 128, 32, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
     assert f(None, 0, None, None, 0, 128, 64, 4, None) == 0
     assert f(None, 0, None, None, 5, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert f(P(0x1004), 0, P(0x2000), P(0x3000), 5, 128, 64, 4, None) == \

@@ -47,6 +47,15 @@ def test_insert_matches_oracle(T, num_blocks, bf16):
         raise AssertionError("%d bytes differ, first at %s" % (len(diff), diff[0].tolist()))
 
 
+@pytest.mark.parametrize("bs", [1, 16, 128])
+def test_insert_other_block_sizes(bs):
+    c = inputs.make_kcache_insert(700, -(-700 // bs) + 3, seed=620 + bs, block_size=bs)
+    say("kcache insert bs=%d" % bs)
+    got = gpu_insert(c)
+    want = oracle_kcache.insert(c.kv_cache, c.k, c.slot_mapping, bs)
+    assert np.array_equal(got, want)
+
+
 def test_rounding_boundaries_on_gpu():
     """Rows whose quotients land on every e4m3fn rounding boundary: the row
     maximum is 448 so the scale is 1 and k / scale = k exactly."""

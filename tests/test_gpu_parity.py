@@ -172,6 +172,40 @@ def test_decode_every_ring_depth(depth):
         assert_parity(out, ref, mag, f"decode_depth{depth}_split{split}")
 
 
+BLOCK_SIZE_CASES = [
+    (3, 2, [700, 130, 3000], 3072),
+    (2, 6, [2000, 7], 2001),
+    (4, 1, [0, 15, 17, 4100], 4160),
+    (2, 3, [1, 2], 130),
+]
+
+
+@pytest.mark.parametrize("bs", [1, 16, 128])
+@pytest.mark.parametrize("B,next_n,ctx,mml", BLOCK_SIZE_CASES,
+                         ids=[f"B{b}-nn{n}-mml{m}" for b, n, _, m in BLOCK_SIZE_CASES])
+def test_decode_other_block_sizes(bs, B, next_n, ctx, mml):
+    """Per-token, 16- and 128-token cache blocks (a step spans 64 blocks, four
+    blocks, or half of one); contexts that end mid-block, shorter than a step,
+    or empty."""
+    d = inputs.make_decode(B, next_n, ctx, mml, seed=330 + bs + mml, block_size=bs, poison=True)
+    say("decode bs=%d B=%d next_n=%d ctx=%s mml=%d" % (bs, B, next_n, ctx, mml))
+    ref, mag, _ = oracle_decode(d)
+    for tun in (None, Tunables(split_kv=3), Tunables(rows_per_block=1, split_kv=1)):
+        out = run_decode(d, tun=tun)
+        assert_parity(out, ref, mag, f"decode_bs{bs}_B{B}_nn{next_n}")
+
+
+@pytest.mark.parametrize("bs", [1, 16, 128])
+def test_block_size_does_not_change_bits(bs):
+    """The same tokens paged through 1-, 16- or 128-token blocks give the
+    64-token layout's output bit for bit (the gather is the only step that
+    changes)."""
+    d64 = inputs.make_decode(3, 4, [900, 64, 2500], 2560, seed=340)
+    d = inputs.make_decode(3, 4, [900, 64, 2500], 2560, seed=340, block_size=bs)
+    assert all(np.array_equal(a, b) for a, b in zip(d64.k_seq, d.k_seq))
+    assert np.array_equal(run_decode(d64), run_decode(d), equal_nan=True)
+
+
 # ---------------------------------------------------------------------------
 # GPU self-invariants (bitwise)
 # ---------------------------------------------------------------------------
