@@ -200,8 +200,8 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  * same slot race (either may win).
  * num_tokens == 0 is a successful no-op.  Negative sizes, a bad k_dtype, NULL
  * or misaligned pointers (k and kv_cache 16-byte, slot_mapping 8-byte) ->
- * MQA_ERR_INVALID_ARG; head_dim != 128 or kv_block_size != 64 ->
- * MQA_ERR_UNSUPPORTED.
+ * MQA_ERR_INVALID_ARG; head_dim != 128 or kv_block_size not 1, 16, 64 or 128
+ * -> MQA_ERR_UNSUPPORTED.
  */
 int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
                                uint8_t *kv_cache, int num_tokens, int head_dim,
