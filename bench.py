@@ -104,7 +104,7 @@ class Workload:
             base = dict(q=dev(host.q), k=dev(host.k), sc=dev(host.kv_scale), w=dev(host.weights),
                         ks=dev(host.ks), ke=dev(host.ke))
             self.out_shape = (host.M, host.N)
-            self.bytes = workload.prefill_essential_bytes(host.M, host.N)
+            self.bytes = workload.prefill_essential_bytes(host.M, host.N, H=host.H)
             self.pairs = workload.prefill_valid_pairs(host.ks, host.ke, host.N)
             set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + host.M * host.N * 4
         else:
@@ -112,13 +112,13 @@ class Workload:
                         ctx=dev(host.context_lens), bt=dev(host.block_tables))
             self.out_shape = (host.B * host.next_n, host.max_model_len)
             self.bytes = workload.decode_essential_bytes(host.B, host.next_n, host.context_lens,
-                                                         host.max_model_len,
+                                                         host.max_model_len, H=host.H,
                                                          block_size=host.block_size)
             self.pairs = workload.decode_valid_pairs(host.next_n, host.context_lens,
                                                      host.max_model_len)
             set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
                 self.out_shape[0] * self.out_shape[1] * 4
-        self.flops = self.pairs * workload.flops_per_pair()
+        self.flops = self.pairs * workload.flops_per_pair(H=host.H)
         nsets = 1 if hot else min(64, max(1, -(-COLD_BYTES // set_bytes)))
         self.sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
         self.outs = [torch.empty(self.out_shape, dtype=torch.float32, device="cuda")
@@ -299,7 +299,8 @@ def cpu_baseline(wl, budget_s=12.0):
             break
     dt = time.time() - t0
     ctx = h.context_lens[done]
-    nbytes = workload.decode_essential_bytes(len(done), h.next_n, ctx, h.max_model_len)
+    nbytes = workload.decode_essential_bytes(len(done), h.next_n, ctx, h.max_model_len, H=h.H,
+                                             block_size=h.block_size)
     return {"value": round(nbytes / dt / 1e12, 8), "unit": "TB/s", "cores": nthreads,
             "kind": "oracle", "cpu": cpu_model(), "seconds": round(dt, 2),
             "sample": "%d of %d sequences (all %d rows each, every position to max_model_len) of %s"
@@ -539,7 +540,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10, 11, 12, 13) if i != args.workload]
     results, head = {}, None
     for idx in order:
         wl = make_workload(idx, args.hot, tun)
@@ -568,9 +569,9 @@ def main():
     elif decode:
         config = {"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
                   "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
-                  "heads": 32, "head_dim": 128, "kv_block_size": h.block_size, "cold": not args.hot}
+                  "heads": h.H, "head_dim": 128, "kv_block_size": h.block_size, "cold": not args.hot}
     else:
-        config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": 32, "head_dim": 128,
+        config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": h.H, "head_dim": 128,
                   "cold": not args.hot}
     line = {
         "metric": "decode essential HBM TB/s (% of 8 TB/s); prefill fp8 TFLOP/s; us/call",

@@ -77,10 +77,12 @@ typedef struct mqa_tunables {
 } mqa_tunables;
 
 /*
- * Support gate (both pages, "Technical Details": the kernels are fixed to 32
- * heads and head_dim 128 on gfx950, and callers route other shapes elsewhere
- * instead of failing).  kv_block_size: 0 asks about prefill, 1, 16, 64 or
- * 128 about paged decode with blocks of that many tokens.  Returns 1 if the current HIP device is gfx950
+ * Support gate (both pages, "Technical Details": callers ask before routing a
+ * shape to these kernels and go elsewhere instead of failing).  Supported:
+ * head_dim 128 with num_heads 32, 64 or 128 (the head counts the issue page
+ * about next_n tiling sweeps).  kv_block_size: 0 asks about prefill; 1, 16,
+ * 64 or 128 about paged decode with blocks of that many tokens (64 only with
+ * 64 or 128 heads).  Returns 1 if the current HIP device is gfx950
  * and the shape is supported, else 0.  Never fails.
  */
 int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);

@@ -78,11 +78,17 @@ int check_device()
     return MQA_OK;
 }
 
+// 32, 64 or 128 index heads (the pages sweep all three); head dim 128; cache
+// blocks of 1, 16, 64 or 128 tokens for decode (0 asks about prefill), 64 only
+// with more than 32 heads.
 bool shape_supported(int num_heads, int head_dim, int kv_block_size)
 {
-    return num_heads == 32 && head_dim == 128 &&
-           (kv_block_size == 0 || kv_block_size == 1 || kv_block_size == 16 ||
-            kv_block_size == 64 || kv_block_size == 128);
+    if (head_dim != 128 || (num_heads != 32 && num_heads != 64 && num_heads != 128))
+        return false;
+    if (num_heads != 32)
+        return kv_block_size == 0 || kv_block_size == 64;
+    return kv_block_size == 0 || kv_block_size == 1 || kv_block_size == 16 ||
+           kv_block_size == 64 || kv_block_size == 128;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -117,13 +123,19 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     if (M < 0 || N < 0)
         return fail(MQA_ERR_INVALID_ARG, "M=%d, N=%d must be >= 0", M, N);
     if (!shape_supported(num_heads, head_dim, 0))
-        return fail(MQA_ERR_UNSUPPORTED, "prefill supports num_heads=32, head_dim=128 (got %d, %d)",
+        return fail(MQA_ERR_UNSUPPORTED,
+                    "prefill supports num_heads 32, 64 or 128 and head_dim 128 (got %d, %d)",
                     num_heads, head_dim);
+    const int head_tiles = num_heads / 32;
+    const int max_block_m = 8 / head_tiles;  // Q and weights of a wave's rows stay in VGPRs
     mqa_tunables t = {};
     if (tun)
         t = *tun;
     if (t.block_m != 0 && t.block_m != 1 && t.block_m != 2 && t.block_m != 4 && t.block_m != 8)
         return fail(MQA_ERR_INVALID_ARG, "block_m must be 0, 1, 2, 4 or 8 (got %d)", t.block_m);
+    if (t.block_m > max_block_m)
+        return fail(MQA_ERR_INVALID_ARG, "block_m is at most %d with %d heads (got %d)", max_block_m,
+                    num_heads, t.block_m);
     if (t.split_n < 0 || t.num_warps < 0 || t.num_warps > 4)
         return fail(MQA_ERR_INVALID_ARG, "split_n >= 0 and num_warps in 0..4 required");
     if (t.reverse_rows < -1 || t.reverse_rows > 1)
@@ -158,7 +170,8 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     // enough column splits for ~2048 workgroups while each wave keeps >= 4
     // steps.  High-m first for long causal chunks (aiter PR 5046 page,
     // "Technical Details": N > 2048).
-    p.block_m = t.block_m ? t.block_m : (M >= 1024 ? 8 : 4);
+    p.head_tiles = head_tiles;
+    p.block_m = t.block_m ? t.block_m : std::min(M >= 1024 ? 8 : 4, max_block_m);
     p.num_warps = t.num_warps ? t.num_warps : (M >= 1024 ? 1 : 4);
     const int64_t nrb = ceil_div(M, p.block_m);
     const int64_t steps = ceil_div(N, 64);
@@ -196,18 +209,22 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
         return fail(MQA_ERR_INVALID_ARG, "next_n must be in 1..8 (got %d)", next_n);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "decode supports num_heads=32, head_dim=128, kv_block_size 1, 16, 64 or 128 "
-                    "(got %d, %d, %d)",
+                    "decode supports num_heads=32 with kv_block_size 1, 16, 64 or 128, or "
+                    "num_heads 64 / 128 with kv_block_size 64; head_dim=128 (got %d, %d, %d)",
                     num_heads, head_dim, kv_block_size);
     mqa_tunables t = {};
     if (tun)
         t = *tun;
-    if (t.rows_per_block < 0 || t.rows_per_block > 4 || t.split_kv < 0 || t.num_warps != 0 ||
-        t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7 ||
-        (kv_block_size != 64 && t.ring_depth != 0 && t.ring_depth != 4))
+    const int head_tiles = num_heads / 32;
+    const int max_rows = 4 / head_tiles;  // Q and weights of a wave's rows stay in VGPRs
+    const bool any_depth = kv_block_size == 64 && head_tiles == 1;
+    if (t.rows_per_block < 0 || t.rows_per_block > max_rows || t.split_kv < 0 ||
+        t.num_warps != 0 || t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7 ||
+        (!any_depth && t.ring_depth != 0 && t.ring_depth != 4))
         return fail(MQA_ERR_INVALID_ARG,
-                    "decode tunables: rows_per_block in 0..4, split_kv >= 0, ring_depth 0 or 2..7 "
-                    "(0 or 4 unless kv_block_size is 64), num_warps 0");
+                    "decode tunables: rows_per_block in 0..%d, split_kv >= 0, ring_depth 0 or 2..7 "
+                    "(0 or 4 unless 32 heads and kv_block_size 64), num_warps 0",
+                    max_rows);
     if (batch == 0 || max_model_len == 0)
         return ok();
     if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables || !logits)
@@ -242,7 +259,8 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     //   split: at least ~1024 workgroups, and at most 32 steps (2048 tokens)
     //          per workgroup at the longest context, but at least 4 steps.
     int rows = t.rows_per_block ? t.rows_per_block : (next_n == 1 ? 1 : (next_n + 1) / 2);
-    rows = std::min(rows, next_n);
+    rows = std::min(std::min(rows, next_n), max_rows);
+    p.head_tiles = head_tiles;
     p.rows = rows;
     p.depth = t.ring_depth ? t.ring_depth : 4;
     p.block_size = kv_block_size;

@@ -236,11 +236,6 @@ __device__ __forceinline__ void wait_vm()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One cache block in the MFMA operand layout: two K tiles and the 64 scales.
-struct KStep {
-    Frag t[2];
-    float sc[2];
-};
 
 // Read a ring slot into registers.  Lane (t, g') needs token 32 h + t,
 // granules u = 2j + g', j = 0..3: chunk c = 4h + t/8 (same parity for both
@@ -281,40 +276,7 @@ __device__ __forceinline__ void read_wait(KStep &k)
                  : "memory");
 }
 
-// Scores, relu.weight sums and kv-scaled head sums for one cache block (two
-// 32-token tiles) and the wave's R rows.  tot[h][i] holds row pair i of tile
-// h: lanes 0..31 row 2i, lanes 32..63 row 2i + 1.  Row-tiles are software
-// pipelined by one: the MFMAs of row-tile i+1 are issued before the
-// relu.weight epilogue of row-tile i, so the epilogue never waits on the MFMA
-// it consumes.
-template <int R>
-__device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[R],
-                                            const Weights16 (&w)[R], float (&tot)[2][(R + 1) / 2])
-{
-    constexpr int NT = 2 * R;
-    float part[2][R];
-    f32x16 prev = row_scores(q[0], k.t[0]);
-#pragma unroll
-    for (int it = 1; it < NT; ++it) {
-        const int h = it / R, r = it % R;
-        const int ph = (it - 1) / R, pr = (it - 1) % R;
-        f32x16 cur = row_scores(q[r], k.t[h]);
-        part[ph][pr] = relu_weight_sum(prev, w[pr]);
-        prev = cur;
-    }
-    part[1][R - 1] = relu_weight_sum(prev, w[R - 1]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < (R + 1) / 2; ++i) {
-            // an odd last row is paired with itself; its upper half is never stored
-            const float pb = (2 * i + 1 < R) ? part[h][(2 * i + 1 < R) ? 2 * i + 1 : 2 * i] : part[h][2 * i];
-            tot[h][i] = pair_head_sum(part[h][2 * i], pb) * k.sc[h];
-        }
-    }
-}
-
-template <int R, int G, int D, int BS>
+template <int R, int G, int D, int BS, int HT>
 __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restrict__ qbuf,
                                                         const uint8_t *__restrict__ cache,
                                                         const float *__restrict__ wbuf,
@@ -348,15 +310,19 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
     const float ninf = -__builtin_inff();
 
     if (st0 < st1) {
-        Frag q[R];
-        Weights16 w[R];
+        constexpr int H = kHeads * HT;
+        Frag q[R][HT];
+        Weights16 w[R][HT];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             // a short last group computes its missing rows as copies of its
             // last row and never stores them, so the loop body stays branch-free
             const int64_t row = row_base + min(r, nrows - 1);
-            load_frag(q[r], qbuf + row * (kHeads * kDim) + t * kDim, lane);
-            load_weights(w[r], wbuf + row * kHeads, lane);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                load_frag(q[r][ht], qbuf + row * (H * kDim) + (ht * kHeads + t) * kDim, lane);
+                load_weights(w[r][ht], wbuf + row * H + ht * kHeads, lane);
+            }
         }
         // This lane's output row (and column t) within each pair, its window
         // bound, and whether the row exists.
@@ -481,7 +447,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
             rd = (rd + 1 == D) ? 0 : rd + 1;
             wr = (wr + 1 == D) ? 0 : wr + 1;
             read_wait(kb);
-            step_scores<R>(kb, q, w, prev_tot);
+            step_scores<R, HT>(kb, q, w, prev_tot);
         }
         store_step(st1 - 1, prev_tot);
         // No global->LDS load may still be in flight once the workgroup ends
@@ -495,11 +461,11 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
     }
 }
 
-template <int R, int G, int D, int BS>
+template <int R, int G, int D, int BS, int HT = 1>
 hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
     const size_t lds = (size_t)D * kSlotBytes + (BS == 1 ? (size_t)(2 * D - 2) * kStep * 4 : 0);
-    hipLaunchKernelGGL((decode_kernel<R, G, D, BS>), dim3(grid), dim3(64 * G), lds, stream, p.q,
+    hipLaunchKernelGGL((decode_kernel<R, G, D, BS, HT>), dim3(grid), dim3(64 * G), lds, stream, p.q,
                        p.cache, p.weights, p.context_lens, p.block_tables, p.logits, a);
     return hipGetLastError();
 }
@@ -543,6 +509,38 @@ hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream)
     a.groups = (p.next_n + p.rows - 1) / p.rows;
     a.split = p.split_kv;
     const int grid = p.batch * a.split;
+    if (p.head_tiles == 2) {
+        // 64 heads: at most 2 rows per wave (Q and weights take 64 VGPRs a row)
+        switch (p.rows * 16 + a.groups) {
+        case 1 * 16 + 1: return launch_rgdb<1, 1, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 2: return launch_rgdb<1, 2, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 3: return launch_rgdb<1, 3, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 4: return launch_rgdb<1, 4, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 5: return launch_rgdb<1, 5, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 6: return launch_rgdb<1, 6, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 7: return launch_rgdb<1, 7, 4, 64, 2>(p, a, grid, stream);
+        case 1 * 16 + 8: return launch_rgdb<1, 8, 4, 64, 2>(p, a, grid, stream);
+        case 2 * 16 + 1: return launch_rgdb<2, 1, 4, 64, 2>(p, a, grid, stream);
+        case 2 * 16 + 2: return launch_rgdb<2, 2, 4, 64, 2>(p, a, grid, stream);
+        case 2 * 16 + 3: return launch_rgdb<2, 3, 4, 64, 2>(p, a, grid, stream);
+        case 2 * 16 + 4: return launch_rgdb<2, 4, 4, 64, 2>(p, a, grid, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (p.head_tiles == 4) {
+        // 128 heads: one row per wave
+        switch (a.groups) {
+        case 1: return launch_rgdb<1, 1, 4, 64, 4>(p, a, grid, stream);
+        case 2: return launch_rgdb<1, 2, 4, 64, 4>(p, a, grid, stream);
+        case 3: return launch_rgdb<1, 3, 4, 64, 4>(p, a, grid, stream);
+        case 4: return launch_rgdb<1, 4, 4, 64, 4>(p, a, grid, stream);
+        case 5: return launch_rgdb<1, 5, 4, 64, 4>(p, a, grid, stream);
+        case 6: return launch_rgdb<1, 6, 4, 64, 4>(p, a, grid, stream);
+        case 7: return launch_rgdb<1, 7, 4, 64, 4>(p, a, grid, stream);
+        case 8: return launch_rgdb<1, 8, 4, 64, 4>(p, a, grid, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     // (rows, row groups) pairs that next_n in 1..8 can produce
     switch (p.rows * 16 + a.groups) {
     case 1 * 16 + 1: return launch_rg<1, 1>(p, a, grid, stream);

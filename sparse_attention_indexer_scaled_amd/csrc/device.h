@@ -121,6 +121,52 @@ __device__ __forceinline__ float pair_head_sum(float a, float b)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One 64-token step of K in the MFMA operand layout: two 32-token tiles and
+// the tokens' scales (lane t of tile h holds the scale of token 32 h + t).
+struct KStep {
+    Frag t[2];
+    float sc[2];
+};
+
+// Scores, relu.weight sums and kv-scaled head sums for one 64-token step and
+// R query rows of 32 HT heads each (q[r][ht], w[r][ht]: head tile ht of row r).
+// tot[h][i] holds row pair i of tile h: lanes 0..31 row 2i, lanes 32..63 row
+// 2i + 1.  The (tile, row, head tile) items are software pipelined by one: the
+// MFMAs of item i+1 are issued before the relu.weight epilogue of item i, so
+// the epilogue never waits on the MFMA it consumes.  A row's head tiles are
+// summed in order; with one head tile the sum is the item itself.
+template <int R, int HT>
+__device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[R][HT],
+                                            const Weights16 (&w)[R][HT],
+                                            float (&tot)[2][(R + 1) / 2])
+{
+    constexpr int NT = 2 * R * HT;
+    float part[2][R];
+    f32x16 prev = row_scores(q[0][0], k.t[0]);
+#pragma unroll
+    for (int it = 1; it <= NT; ++it) {
+        f32x16 cur = prev;
+        if (it < NT) {
+            const int h = it / (R * HT), r = (it / HT) % R, ht = it % HT;
+            cur = row_scores(q[r][ht], k.t[h]);
+        }
+        const int pit = it - 1;
+        const int ph = pit / (R * HT), pr = (pit / HT) % R, pht = pit % HT;
+        const float v = relu_weight_sum(prev, w[pr][pht]);
+        part[ph][pr] = pht == 0 ? v : part[ph][pr] + v;
+        prev = cur;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < (R + 1) / 2; ++i) {
+            // an odd last row is paired with itself; its upper half is never stored
+            const float pb = part[h][(2 * i + 1 < R) ? 2 * i + 1 : 2 * i];
+            tot[h][i] = pair_head_sum(part[h][2 * i], pb) * k.sc[h];
+        }
+    }
+}
+
 // Write -inf over row[c0, c1), split into `nparts` contiguous parts of which
 // this wave writes part `part`.  16-byte stores where alignment allows.
 __device__ __forceinline__ void fill_neg_inf(float *row, int64_t c0, int64_t c1, int part,

@@ -22,6 +22,7 @@ struct PrefillLaunch {
     int split_n;   // workgroups per row block
     int num_warps; // waves per workgroup
     int reverse;   // 1: high-m row blocks first
+    int head_tiles;  // num_heads / 32: 1, 2 or 4
 };
 
 struct DecodeLaunch {
@@ -41,6 +42,7 @@ struct DecodeLaunch {
     int depth;     // 64-token steps in each workgroup's LDS ring, 2..7 (at most 64 KiB);
                    // 4 for block sizes other than 64
     int block_size;  // tokens per cache block: 1, 16, 64 or 128
+    int head_tiles;  // num_heads / 32: 1, 2 or 4 (2 and 4: block size 64, depth 4)
 };
 
 // Largest k of the row-wise top-k.

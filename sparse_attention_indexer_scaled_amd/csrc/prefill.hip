@@ -39,10 +39,6 @@ struct PrefillArgs {
     int reverse;
 };
 
-struct KStep {
-    Frag t[2];
-    float sc[2];
-};
 
 // Step starting at column n0.  Rows past N are clamped to N - 1: the load stays
 // in bounds and the column is never stored.
@@ -58,42 +54,7 @@ __device__ __forceinline__ void load_kstep(KStep &k, const uint8_t *kbuf, const 
     k.sc[1] = scale[n_b];
 }
 
-// Scores, relu.weight sums and kv-scaled head sums for one 64-column step and
-// the wave's BM rows; tot[h][i] is row pair i of tile h (lanes 0..31 row 2i,
-// lanes 32..63 row 2i + 1).  Branch-free so one row's epilogue (VALU) can
-// overlap the next row's MFMAs.
-template <int BM>
-__device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[BM],
-                                            const Weights16 (&w)[BM], float (&tot)[2][(BM + 1) / 2])
-{
-    // Row-tiles in the order (tile 0: rows 0..BM-1, tile 1: rows 0..BM-1), software
-    // pipelined by one: the MFMAs of row-tile i+1 are issued before the
-    // relu.weight epilogue of row-tile i, so the epilogue never waits for the
-    // MFMA it consumes and the matrix core has work queued meanwhile.
-    constexpr int NT = 2 * BM;
-    float part[2][BM];
-    f32x16 prev = row_scores(q[0], k.t[0]);
-#pragma unroll
-    for (int it = 1; it < NT; ++it) {
-        const int h = it / BM, r = it % BM;
-        const int ph = (it - 1) / BM, pr = (it - 1) % BM;
-        f32x16 cur = row_scores(q[r], k.t[h]);
-        part[ph][pr] = relu_weight_sum(prev, w[pr]);
-        prev = cur;
-    }
-    part[1][BM - 1] = relu_weight_sum(prev, w[BM - 1]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < (BM + 1) / 2; ++i) {
-            // an odd last row is paired with itself; its upper half is never stored
-            const float pb = (2 * i + 1 < BM) ? part[h][(2 * i + 1 < BM) ? 2 * i + 1 : 2 * i] : part[h][2 * i];
-            tot[h][i] = pair_head_sum(part[h][2 * i], pb) * k.sc[h];
-        }
-    }
-}
-
-template <int BM>
+template <int BM, int HT>
 __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict__ qbuf,
                                                       const uint8_t *__restrict__ kbuf,
                                                       const float *__restrict__ scale,
@@ -156,13 +117,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
 
     int st = st0 + wave;
     if (st < st1) {
-        Frag q[BM];
-        Weights16 w[BM];
+        constexpr int H = kHeads * HT;
+        Frag q[BM][HT];
+        Weights16 w[BM][HT];
 #pragma unroll
         for (int r = 0; r < BM; ++r) {
             const int64_t row = m0 + min(r, nrows - 1);
-            load_frag(q[r], qbuf + row * (kHeads * kDim) + t * kDim, lane);
-            load_weights(w[r], wbuf + row * kHeads, lane);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                load_frag(q[r][ht], qbuf + row * (H * kDim) + (ht * kHeads + t) * kDim, lane);
+                load_weights(w[r][ht], wbuf + row * H + ht * kHeads, lane);
+            }
         }
         auto store_step = [&](int step, const float (&tot)[2][NP]) {
 #pragma unroll
@@ -186,14 +151,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
             load_kstep(B, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
             __builtin_amdgcn_sched_barrier(0);
             float tot[2][NP];
-            step_scores<BM>(A, q, w, tot);
+            step_scores<BM, HT>(A, q, w, tot);
             store_step(st, tot);
             st += nw;
             if (st >= st1)
                 break;
             load_kstep(A, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
             __builtin_amdgcn_sched_barrier(0);
-            step_scores<BM>(B, q, w, tot);
+            step_scores<BM, HT>(B, q, w, tot);
             store_step(st, tot);
             st += nw;
             if (st >= st1)
@@ -212,11 +177,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
     }
 }
 
-template <int BM>
+template <int BM, int HT = 1>
 hipError_t launch_bm(const PrefillLaunch &p, const PrefillArgs &a, int grid, int block,
                      hipStream_t stream)
 {
-    hipLaunchKernelGGL(prefill_kernel<BM>, dim3(grid), dim3(block), 0, stream, p.q, p.k,
+    hipLaunchKernelGGL((prefill_kernel<BM, HT>), dim3(grid), dim3(block), 0, stream, p.q, p.k,
                        p.kv_scale, p.weights, p.ks, p.ke, p.logits, a);
     return hipGetLastError();
 }
@@ -234,6 +199,21 @@ hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream)
     a.reverse = p.reverse;
     const int grid = a.nrb * a.split;
     const int block = 64 * p.num_warps;
+    if (p.head_tiles == 2) {  // 64 heads: at most 4 rows per wave
+        switch (p.block_m) {
+        case 1: return launch_bm<1, 2>(p, a, grid, block, stream);
+        case 2: return launch_bm<2, 2>(p, a, grid, block, stream);
+        case 4: return launch_bm<4, 2>(p, a, grid, block, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (p.head_tiles == 4) {  // 128 heads: at most 2 rows per wave
+        switch (p.block_m) {
+        case 1: return launch_bm<1, 4>(p, a, grid, block, stream);
+        case 2: return launch_bm<2, 4>(p, a, grid, block, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.block_m) {
     case 1: return launch_bm<1>(p, a, grid, block, stream);
     case 2: return launch_bm<2>(p, a, grid, block, stream);

@@ -300,6 +300,13 @@ CONFIGS = {
             mml=131072, block_size=16),
     10: dict(kind="decode", name="decode_B16_nn6_ctx131072_bs1", B=16, next_n=6, ctx=131072,
              mml=131072, block_size=1),
+    # the headline decode shape and the long prefill chunk with 64 and 128
+    # index heads (the same K bytes, more contraction per byte)
+    11: dict(kind="decode", name="decode_B16_nn6_ctx131072_h64", B=16, next_n=6, ctx=131072,
+             mml=131072, H=64),
+    12: dict(kind="decode", name="decode_B16_nn6_ctx131072_h128", B=16, next_n=6, ctx=131072,
+             mml=131072, H=128),
+    13: dict(kind="prefill", name="prefill_M4096_N32768_h64", M=4096, N=32768, H=64),
 }
 
 
@@ -308,10 +315,10 @@ def make_config(idx: int, poison: bool = False):
     c = CONFIGS[idx]
     seed = 1000 + idx
     if c["kind"] == "prefill":
-        return make_prefill(c["M"], c["N"], seed)
+        return make_prefill(c["M"], c["N"], seed, H=c.get("H", HEADS))
     return make_decode(c["B"], c["next_n"], c["ctx"], c["mml"], seed,
                        ctx_range=c.get("ctx_range"), poison=poison,
-                       block_size=c.get("block_size", KV_BLOCK))
+                       block_size=c.get("block_size", KV_BLOCK), H=c.get("H", HEADS))
 
 
 # Row families for the top-k over logits: shapes a logits row takes (a masked
