@@ -255,21 +255,25 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     //         rows share one HBM stream whatever the row split; 2 waves per
     //         workgroup (e.g. next_n 6 -> 2 x 3 rows) keep each wave within 256
     //         registers, 2 waves per SIMD.
-    //   depth: 4 blocks (33 KiB) per workgroup, 4 workgroups per CU.
+    //   depth: 3 steps (25 KiB) per workgroup for 64-token blocks and 32
+    //          heads (the other layouts instantiate 4 only); deeper rings cost
+    //          workgroups per CU and measured slower.
     //   split: at least ~1024 workgroups, and at most 32 steps (2048 tokens)
-    //          per workgroup at the longest context, but at least 4 steps.
+    //          per workgroup at the longest context, but at least 2 steps;
+    //          more workgroups per sequence than that measured slower (longer
+    //          prologues relative to the work, more concurrent streams).
     int rows = t.rows_per_block ? t.rows_per_block : (next_n == 1 ? 1 : (next_n + 1) / 2);
     rows = std::min(std::min(rows, next_n), max_rows);
     p.head_tiles = head_tiles;
     p.rows = rows;
-    p.depth = t.ring_depth ? t.ring_depth : 4;
+    p.depth = t.ring_depth ? t.ring_depth : (any_depth ? 3 : 4);
     p.block_size = kv_block_size;
     const int64_t steps_max = ceil_div(max_model_len, 64);
     if (t.split_kv) {
         p.split_kv = t.split_kv;
     } else {
         const int64_t want = std::max(ceil_div(1024, batch), ceil_div(steps_max, 32));
-        const int64_t cap = std::max<int64_t>(1, steps_max / 4);
+        const int64_t cap = std::max<int64_t>(1, steps_max / 2);
         p.split_kv = (int)std::max<int64_t>(1, std::min(want, cap));
     }
     if ((int64_t)batch * p.split_kv > INT32_MAX)
