@@ -293,7 +293,8 @@ def cpu_baseline(wl, budget_s=12.0):
     done, t0 = [], time.time()
     for b in range(h.B):
         oracle.decode(h.q[b:b + 1], h.kv_cache, h.weights[b * h.next_n:(b + 1) * h.next_n],
-                      h.context_lens[b:b + 1], h.block_tables[b:b + 1], h.max_model_len, h.block_size)
+                      h.context_lens[b:b + 1], h.block_tables[b:b + 1], h.max_model_len, h.block_size,
+                      preshuffle=h.preshuffle)
         done.append(b)
         if time.time() - t0 > budget_s:
             break

@@ -57,8 +57,8 @@ def _load():
         lib.oracle_set_num_threads.argtypes = [i32]
         lib.oracle_prefill.argtypes = [P, P, P, P, P, P, i64, i64, i32, i32, i32, i32, P]
         lib.oracle_decode.restype = i32
-        lib.oracle_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i64, i32, i64,
-                                      i32, i32, P]
+        lib.oracle_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, i32,
+                                      i64, i32, i32, P]
         _lib = lib
     return _lib
 
@@ -114,12 +114,13 @@ def prefill(q, k, kv_scale, weights, ks, ke, clean=True, hoist=False, out=None) 
 
 
 def decode(q, kv_cache, weights, context_lens, block_tables, max_model_len, block_size,
-           clean=True, hoist=False, out=None) -> np.ndarray:
+           clean=True, hoist=False, out=None, preshuffle=False) -> np.ndarray:
     """Oracle paged-decode logits (float64 [B*next_n, max_model_len]).
 
     q uint8 [B,next_n,H,D], kv_cache uint8 [num_blocks, block_size*(D+4)],
     weights f32 [B*next_n,H], context_lens int32 [B], block_tables int32
-    [B, max_blocks_per_seq].
+    [B, max_blocks_per_seq].  preshuffle: the K rows of each block are in the
+    16 x 16-byte tiled order (see ``oracle_decode``) instead of slot-major.
     """
     q = _c(q, np.uint8)
     B, next_n, H, D = q.shape
@@ -138,8 +139,10 @@ def decode(q, kv_cache, weights, context_lens, block_tables, max_model_len, bloc
         out = np.empty((B * next_n, max_model_len), dtype=np.float64)
     assert out.dtype == np.float64 and out.shape == (B * next_n, max_model_len)
     rc = _load().oracle_decode(_ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(ctx), _ptr(bt), B,
-                               next_n, H, D, block_size, num_blocks, mbps, max_model_len,
-                               int(bool(clean)), int(bool(hoist)), _ptr(out))
+                               next_n, H, D, block_size, int(bool(preshuffle)), num_blocks, mbps,
+                               max_model_len, int(bool(clean)), int(bool(hoist)), _ptr(out))
+    if rc == -2:
+        raise ValueError("the tiled layout needs block_size and head_dim multiples of 16")
     if rc != 0:
         raise ValueError("block table entry out of range for a position inside a window")
     return out

@@ -70,9 +70,14 @@ def quantize_tokens(k: np.ndarray):
     return e4m3fn_rne(q), scale
 
 
-def insert(kv_cache: np.ndarray, k: np.ndarray, slot_mapping: np.ndarray, block_size: int):
+def insert(kv_cache: np.ndarray, k: np.ndarray, slot_mapping: np.ndarray, block_size: int,
+           preshuffle: bool = False):
     """Return a copy of kv_cache [num_blocks, bs*(D+4)] bytes with the tokens
-    of k [T, D] quantised into their slots (slot < 0: token skipped)."""
+    of k [T, D] quantised into their slots (slot < 0: token skipped).
+
+    preshuffle: the K rows of a block are in 16 x 16-byte tiles (the decode
+    oracle's layout 1): byte d of slot s at (s/16)*16*D + (d/16)*256 +
+    (s%16)*16 + d%16; otherwise slot-major, byte d of slot s at s*D + d."""
     cache = np.array(kv_cache, dtype=np.uint8, copy=True)
     T, D = k.shape
     codes, scale = quantize_tokens(k)
@@ -82,7 +87,12 @@ def insert(kv_cache: np.ndarray, k: np.ndarray, slot_mapping: np.ndarray, block_
         if s < 0:
             continue
         blk, slot = divmod(s, block_size)
-        flat[blk, slot * D:(slot + 1) * D] = codes[t]
+        if preshuffle:
+            for d in range(D):
+                flat[blk, (slot // 16) * 16 * D + (d // 16) * 256 + (slot % 16) * 16 + d % 16] = \
+                    codes[t, d]
+        else:
+            flat[blk, slot * D:(slot + 1) * D] = codes[t]
         off = block_size * D + 4 * slot
         flat[blk, off:off + 4] = np.frombuffer(np.float32(scale[t]).tobytes(), dtype=np.uint8)
     return cache

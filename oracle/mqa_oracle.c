@@ -146,19 +146,28 @@ void oracle_prefill(const uint8_t *q, const uint8_t *k, const float *kv_scale,
  * b covers KV positions p <= context_lens[b] - next_n + j (the issue page on
  * next_n tiling names the same bound "context_length - next_n + pid_next_n").
  * K and its per-token scale are read through block_tables; the cache layout is
- * block-split: block i is bs*(D+4) bytes, K rows of its bs slots first
- * (slot-major, D bytes each), then the bs fp32 scales.
+ * block-split: block i is bs*(D+4) bytes, K rows of its bs slots first, then
+ * the bs fp32 scales.  The K rows are either slot-major (layout 0: slot s's D
+ * bytes at s*D) or tiled in 16 x 16 byte tiles (layout 1, the preshuffled
+ * (16,16) cache the aiter PR 5047 page names under "Technical Details" for
+ * 64-token blocks): the slots form groups of 16, group by group, each group
+ * holding its 16-byte column granules in order, each granule holding the 16
+ * slots' bytes of that granule one slot after the other.  So byte d of slot s
+ * sits at  (s/16)*16*D + (d/16)*256 + (s%16)*16 + d%16.
  *
  * q [B,next_n,H,D], w [B*next_n,H], ctx [B], bt [B,mbps], out [B*next_n, mml].
- * Returns 0, or -1 if a table entry that has to be read is out of range.
+ * Returns 0, -1 if a table entry that has to be read is out of range, or -2
+ * for a layout the block shape cannot hold.
  */
 int oracle_decode(const uint8_t *q, const uint8_t *cache, const float *w,
                   const int32_t *ctx, const int32_t *bt, int B, int next_n,
-                  int H, int D, int bs, int64_t num_blocks, int mbps,
+                  int H, int D, int bs, int layout, int64_t num_blocks, int mbps,
                   int64_t mml, int clean, int hoist, double *out)
 {
     ensure_table();
     int bad = 0;
+    if (layout != 0 && (layout != 1 || bs % 16 != 0 || D % 16 != 0 || D > 1024))
+        return -2;
     int64_t block_bytes = (int64_t)bs * (D + 4);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int64_t row = 0; row < (int64_t)B * next_n; ++row) {
@@ -182,7 +191,15 @@ int oracle_decode(const uint8_t *q, const uint8_t *cache, const float *w,
                 int64_t slot = p % bs;
                 float sc;
                 memcpy(&sc, base + (int64_t)bs * D + slot * 4, 4);
-                *o = one_logit(q + row * H * D, base + slot * D, (double)sc,
+                const uint8_t *krow = base + slot * D;
+                uint8_t tiled[1024];
+                if (layout == 1) {
+                    for (int d = 0; d < D; ++d)
+                        tiled[d] = base[(slot / 16) * 16 * D + (d / 16) * 256 +
+                                        (slot % 16) * 16 + d % 16];
+                    krow = tiled;
+                }
+                *o = one_logit(q + row * H * D, krow, (double)sc,
                                w + row * H, H, D, hoist);
             } else if (clean) {
                 *o = -INFINITY;

@@ -193,6 +193,8 @@ class DecodeInputs:
     # the same K and scales, unpaged: k_seq[b] is uint8 [ctx_b, D]
     k_seq: list
     s_seq: list
+    # K rows of each block in the (16,16)-tiled order (see preshuffle_blocks)
+    preshuffle: bool = False
 
     @property
     def B(self):
@@ -223,10 +225,22 @@ def cache_views(cache: np.ndarray, block_size: int, D: int):
     return kview, sview
 
 
+def preshuffle_blocks(cache: np.ndarray, block_size: int, D: int) -> np.ndarray:
+    """The same blocks with their K rows rearranged into the preshuffled (16,16)
+    order: a block's slots in groups of 16; within a group, 16-byte column
+    granule u of all 16 slots (slot by slot) before granule u + 1.  Scales are
+    unchanged.  A pure byte permutation."""
+    nb = cache.shape[0]
+    out = cache.copy()
+    k = cache[:, : block_size * D].reshape(nb, block_size // 16, 16, D // 16, 16)
+    out[:, : block_size * D] = k.transpose(0, 1, 3, 2, 4).reshape(nb, block_size * D)
+    return out
+
+
 def make_decode(B: int, next_n: int, context_lens, max_model_len: int, seed: int,
                 H: int = HEADS, D: int = HEAD_DIM, block_size: int = KV_BLOCK,
                 ctx_range: Optional[Sequence[int]] = None, poison: bool = False,
-                extra_table_cols: int = 0) -> DecodeInputs:
+                extra_table_cols: int = 0, preshuffle: bool = False) -> DecodeInputs:
     """Build one paged-decode input set.
 
     ``context_lens``: an int (uniform), a sequence of B ints, or None together
@@ -236,6 +250,8 @@ def make_decode(B: int, next_n: int, context_lens, max_model_len: int, seed: int
     seeded random order, plus (with ``poison``) one extra block of NaN bytes
     that every unused table lane points to.  Slots past a sequence's context
     hold NaN bytes (K code 0x7F, scale NaN) with ``poison``, zeros otherwise.
+    ``preshuffle`` stores each block's K rows in the (16,16)-tiled order; the
+    draws are the same, so the logical K is the same as without it.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     if context_lens is None:
@@ -280,7 +296,10 @@ def make_decode(B: int, next_n: int, context_lens, max_model_len: int, seed: int
         p = np.arange(c)
         kview[phys[p // block_size], p % block_size] = k_seq[b]
         sview[phys[p // block_size], p % block_size] = s_seq[b]
-    return DecodeInputs(q, cache, w, ctx, tables, int(max_model_len), block_size, k_seq, s_seq)
+    if preshuffle:
+        cache = preshuffle_blocks(cache, block_size, D)
+    return DecodeInputs(q, cache, w, ctx, tables, int(max_model_len), block_size, k_seq, s_seq,
+                        preshuffle)
 
 
 # ---------------------------------------------------------------------------
@@ -307,6 +326,9 @@ CONFIGS = {
     12: dict(kind="decode", name="decode_B16_nn6_ctx131072_h128", B=16, next_n=6, ctx=131072,
              mml=131072, H=128),
     13: dict(kind="prefill", name="prefill_M4096_N32768_h64", M=4096, N=32768, H=64),
+    # the headline decode shape in the preshuffled (16,16) 64-token cache
+    14: dict(kind="decode", name="decode_B16_nn6_ctx131072_preshuffle", B=16, next_n=6,
+             ctx=131072, mml=131072, preshuffle=True),
 }
 
 
@@ -318,7 +340,8 @@ def make_config(idx: int, poison: bool = False):
         return make_prefill(c["M"], c["N"], seed, H=c.get("H", HEADS))
     return make_decode(c["B"], c["next_n"], c["ctx"], c["mml"], seed,
                        ctx_range=c.get("ctx_range"), poison=poison,
-                       block_size=c.get("block_size", KV_BLOCK), H=c.get("H", HEADS))
+                       block_size=c.get("block_size", KV_BLOCK), H=c.get("H", HEADS),
+                       preshuffle=c.get("preshuffle", False))
 
 
 # Row families for the top-k over logits: shapes a logits row takes (a masked

@@ -93,9 +93,9 @@ def oracle_decode(d, seqs=None):
     rows = (b[:, None] * d.next_n + np.arange(d.next_n)[None, :]).reshape(-1)
     ctx, bt = d.context_lens[b], d.block_tables[b]
     ref = oracle.decode(d.q[b], d.kv_cache, d.weights[rows], ctx, bt, d.max_model_len,
-                        d.block_size)
+                        d.block_size, preshuffle=d.preshuffle)
     mag = oracle.decode(_abs8(d.q[b]), _abs8_cache(d), np.abs(d.weights[rows]), ctx, bt,
-                        d.max_model_len, d.block_size)
+                        d.max_model_len, d.block_size, preshuffle=d.preshuffle)
     return ref, mag, rows
 
 

@@ -335,3 +335,83 @@ def test_unowned_cache_slots_do_not_leak():
     d = inputs.make_decode(2, 2, [65, 130], 200, seed=101, poison=True)
     out = oracle.decode(d.q, d.kv_cache, d.weights, d.context_lens, d.block_tables, 200, 64)
     assert not np.isnan(out).any()
+
+
+# ---------------------------------------------------------------------------
+# the preshuffled (16,16) cache layout (reading of the aiter PR 5047 page,
+# "Technical Details"; positions worked out by hand in the golden file)
+# ---------------------------------------------------------------------------
+
+
+def _layout_rows():
+    rows = []
+    with open(golden_path("preshuffle_layout.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(tuple(int(x) for x in line.split()))
+    return rows
+
+
+def _one_hot_decode(bs, D, offset, byte, preshuffle):
+    """Decode oracle over one block whose only nonzero K byte (1.0) sits at
+    `offset`, with one head whose query is 1.0 at `byte`: the logit is 1 at
+    the slot that byte belongs to and 0 at every other slot."""
+    cache = np.zeros((1, bs * (D + 4)), dtype=np.uint8)
+    cache[0, offset] = 0x38
+    cache[0, bs * D:] = np.frombuffer(np.ones(bs, np.float32).tobytes(), dtype=np.uint8)
+    q = np.zeros((1, 1, 1, D), dtype=np.uint8)
+    q[0, 0, 0, byte] = 0x38
+    w = np.ones((1, 1), dtype=np.float32)
+    return oracle.decode(q, cache, w, np.array([bs], np.int32), np.zeros((1, 1), np.int32), bs,
+                         bs, preshuffle=preshuffle)[0]
+
+
+@pytest.mark.parametrize("row", _layout_rows(), ids=lambda r: "bs%d-off%d" % (r[0], r[2]))
+def test_preshuffle_positions_worked_by_hand(row):
+    bs, D, offset, slot, byte = row
+    out = _one_hot_decode(bs, D, offset, byte, preshuffle=True)
+    want = np.zeros(bs)
+    want[slot] = 1.0
+    assert np.array_equal(out, want)
+    # the slot-major layout puts that byte at slot * D + byte instead
+    out = _one_hot_decode(bs, D, slot * D + byte, byte, preshuffle=False)
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("row", _layout_rows(), ids=lambda r: "bs%d-off%d" % (r[0], r[2]))
+def test_generator_preshuffle_matches_hand_positions(row):
+    bs, D, offset, slot, byte = row
+    plain = np.zeros((1, bs * (D + 4)), dtype=np.uint8)
+    plain[0, slot * D + byte] = 1
+    tiled = inputs.preshuffle_blocks(plain, bs, D)
+    assert int(np.flatnonzero(tiled[0])[0]) == offset and int(tiled.sum()) == 1
+
+
+@pytest.mark.parametrize("bs", [16, 64, 128])
+def test_preshuffled_decode_equals_plain_decode(bs):
+    """Invariant: the layout moves bytes, not values, so the oracle's logits on
+    the preshuffled cache equal those on the slot-major cache of the same
+    draws, bit for bit (ragged contexts, shuffled table, NaN-poisoned slots)."""
+    kw = dict(B=3, next_n=3, context_lens=[5, bs + 7, 2 * bs], max_model_len=2 * bs + 8, seed=77,
+              H=4, block_size=bs, poison=True)
+    a = inputs.make_decode(**kw)
+    b = inputs.make_decode(preshuffle=True, **kw)
+    assert not np.array_equal(a.kv_cache, b.kv_cache)
+    ra = oracle.decode(a.q, a.kv_cache, a.weights, a.context_lens, a.block_tables,
+                       a.max_model_len, bs)
+    rb = oracle.decode(b.q, b.kv_cache, b.weights, b.context_lens, b.block_tables,
+                       b.max_model_len, bs, preshuffle=True)
+    assert np.array_equal(ra, rb)
+    # and reading the tiled bytes as if slot-major gives something else
+    rc = oracle.decode(b.q, b.kv_cache, b.weights, b.context_lens, b.block_tables,
+                       b.max_model_len, bs)
+    assert not np.array_equal(np.nan_to_num(ra), np.nan_to_num(rc))
+
+
+def test_preshuffle_needs_whole_tiles():
+    q = np.zeros((1, 1, 1, 128), np.uint8)
+    cache = np.zeros((1, 8 * 132), np.uint8)
+    with pytest.raises(ValueError):
+        oracle.decode(q, cache, np.ones((1, 1), np.float32), np.array([8], np.int32),
+                      np.zeros((1, 1), np.int32), 8, 8, preshuffle=True)

@@ -12,7 +12,7 @@ import torch
 import oracle
 from oracle import kcache
 from sparse_attention_indexer_scaled_amd import inputs
-from tests.util import read_kv
+from tests.util import golden_path, read_kv
 
 
 def _golden():
@@ -106,3 +106,33 @@ def test_padding_slots_write_nothing():
     k = rng.standard_normal((3, 128)).astype(np.float32)
     out = kcache.insert(cache, k, np.array([-1, -1, -5], np.int64), 64)
     assert np.array_equal(out, cache)
+
+
+def test_preshuffled_insert_positions_worked_by_hand():
+    """A token that is 448 at one position and 0 elsewhere quantises to scale 1
+    and the code 0x7E there (the largest e4m3fn value); inserted into a
+    preshuffled cache, that code lands at the hand-worked offset of
+    tests/golden/preshuffle_layout.txt and nowhere else."""
+    with open(golden_path("preshuffle_layout.txt")) as f:
+        rows = [tuple(int(x) for x in l.split("#", 1)[0].split()) for l in f
+                if l.split("#", 1)[0].strip()]
+    for bs, D, offset, slot, byte in rows:
+        k = np.zeros((1, D), np.float32)
+        k[0, byte] = 448.0
+        cache = np.zeros((2, bs * (D + 4)), np.uint8)
+        out = kcache.insert(cache, k, np.array([bs + slot], np.int64), bs, preshuffle=True)
+        assert not out[0].any()
+        kpart = out[1, : bs * D]
+        assert np.flatnonzero(kpart).tolist() == [offset] and kpart[offset] == 0x7E
+        assert out[1, bs * D + 4 * slot: bs * D + 4 * slot + 4].view(np.float32)[0] == 1.0
+
+
+@pytest.mark.parametrize("bs", [16, 64, 128])
+def test_preshuffled_insert_is_the_permuted_plain_insert(bs):
+    """The generator's block permutation (numpy reshape/transpose) applied to
+    the slot-major insert gives the preshuffled insert, byte for byte."""
+    d = inputs.make_kcache_insert(40, 4, seed=5, block_size=bs)
+    plain = kcache.insert(d.kv_cache, d.k, d.slot_mapping, bs)
+    tiled_prior = inputs.preshuffle_blocks(d.kv_cache, bs, 128)
+    tiled = kcache.insert(tiled_prior, d.k, d.slot_mapping, bs, preshuffle=True)
+    assert np.array_equal(tiled, inputs.preshuffle_blocks(plain, bs, 128))
