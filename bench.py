@@ -136,7 +136,7 @@ class Workload:
         else:
             paged_mqa_logits_decode(s["q"], s["cache"], s["w"], s["ctx"], s["bt"],
                                     self.host.max_model_len, kv_block_size=self.host.block_size,
-                                    logits=out, tunables=self.tun)
+                                    logits=out, tunables=self.tun, preshuffle=self.host.preshuffle)
 
 
 class TopkWorkload:
@@ -541,7 +541,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10, 11, 12, 13) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14) if i != args.workload]
     results, head = {}, None
     for idx in order:
         wl = make_workload(idx, args.hot, tun)

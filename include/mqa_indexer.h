@@ -115,6 +115,23 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
                        hipStream_t stream);
 
 /*
+ * Order of the K rows inside a cache block (kv_layout argument):
+ *   MQA_KV_SLOT_MAJOR   slot s's head_dim bytes at byte s * head_dim of the
+ *                       block
+ *   MQA_KV_PRESHUFFLED  the preshuffled (16,16) cache that the aiter PR 5047
+ *                       page ("Technical Details") pairs with 64-token blocks:
+ *                       the block's slots in groups of 16; a group stores
+ *                       16-byte column granule u (bytes 16u..16u+15 of each
+ *                       row) of its 16 slots, slot by slot, before granule
+ *                       u + 1.  Byte d of slot s is at
+ *                       (s/16)*16*head_dim + (d/16)*256 + (s%16)*16 + d%16.
+ *                       Needs kv_block_size 16, 64 or 128.
+ * The scales follow the K rows in slot order in both layouts.
+ */
+#define MQA_KV_SLOT_MAJOR 0
+#define MQA_KV_PRESHUFFLED 1
+
+/*
  * Paged decode logits (aiter PR 5047 page, "Motivation" and "Technical
  * Details"; the next_n row bound is also spelled out on the issue page about
  * next_n tiling, "The ask").
@@ -123,11 +140,11 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  *   kv_cache     [num_blocks] blocks of kv_block_size * (head_dim + 4) bytes.
  *                Block i starts at byte i * kv_block_size * (head_dim + 4); its
  *                first kv_block_size * head_dim bytes are the fp8 K rows of
- *                its slots (slot s at byte s * head_dim), the remaining
- *                kv_block_size * 4 bytes the slots' fp32 dequant scales (slot
- *                s at byte kv_block_size * head_dim + 4 s).  For 64-token
- *                blocks a block is 8448 bytes, so every K row stays 16-byte
- *                aligned.
+ *                its slots in the order kv_layout names (slot-major: slot s at
+ *                byte s * head_dim), the remaining kv_block_size * 4 bytes the
+ *                slots' fp32 dequant scales (slot s at byte
+ *                kv_block_size * head_dim + 4 s).  For 64-token blocks a block
+ *                is 8448 bytes, so every K row stays 16-byte aligned.
  *   weights      [batch * next_n, num_heads]  fp32
  *   context_lens [batch]                      int32
  *   block_tables [batch, max_blocks_per_seq]  int32; entry (b, i) is the
@@ -146,17 +163,19 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
  * kv_block_size 1, 16, 64 or 128 (ring_depth tunable other than 4 only with
- * 64).
+ * 64 and 32 heads).  kv_layout MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED (the
+ * latter not with kv_block_size 1).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
- * negative sizes, NULL or misaligned pointers -> MQA_ERR_INVALID_ARG; a shape
- * or block size outside the gate -> MQA_ERR_UNSUPPORTED.
+ * a bad kv_layout, negative sizes, NULL or misaligned pointers ->
+ * MQA_ERR_INVALID_ARG; a shape, block size or layout outside the gate ->
+ * MQA_ERR_UNSUPPORTED.
  */
 int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *weights,
                             const int32_t *context_lens, const int32_t *block_tables,
                             float *logits, int batch, int next_n, int num_heads, int head_dim,
-                            int kv_block_size, int num_blocks, int max_blocks_per_seq,
-                            int max_model_len, int clean_logits, const mqa_tunables *tun,
-                            hipStream_t stream);
+                            int kv_block_size, int kv_layout, int num_blocks,
+                            int max_blocks_per_seq, int max_model_len, int clean_logits,
+                            const mqa_tunables *tun, hipStream_t stream);
 
 /*
  * Row-wise top-k of a logits matrix: the selection that consumes the indexer
@@ -192,7 +211,8 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  *   slot_mapping  [num_tokens]            int64: the cache slot of each token,
  *                                         block * kv_block_size + slot;
  *                                         negative = padding, nothing written
- *   kv_cache      [num_blocks] blocks in the decode layout, updated in place
+ *   kv_cache      [num_blocks] blocks in the decode layout (K rows in the
+ *                 order kv_layout names), updated in place
  *
  * Per token: scale = fp32(max(amax, 1e-12) / 448) (one correctly rounded
  * division), codes = e4m3fn(clamp(k / scale, -448, 448)) rounded to nearest,
@@ -200,14 +220,16 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  * written to its slot; nothing else in the cache changes.  Slots at or past
  * num_blocks * kv_block_size are skipped as well.  Two tokens mapped to the
  * same slot race (either may win).
- * num_tokens == 0 is a successful no-op.  Negative sizes, a bad k_dtype, NULL
- * or misaligned pointers (k and kv_cache 16-byte, slot_mapping 8-byte) ->
- * MQA_ERR_INVALID_ARG; head_dim != 128 or kv_block_size not 1, 16, 64 or 128
- * -> MQA_ERR_UNSUPPORTED.
+ * num_tokens == 0 is a successful no-op.  Negative sizes, a bad k_dtype or
+ * kv_layout, NULL or misaligned pointers (k and kv_cache 16-byte,
+ * slot_mapping 8-byte) -> MQA_ERR_INVALID_ARG; head_dim != 128, kv_block_size
+ * not 1, 16, 64 or 128, or the preshuffled layout with kv_block_size 1 ->
+ * MQA_ERR_UNSUPPORTED.
  */
 int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
                                uint8_t *kv_cache, int num_tokens, int head_dim,
-                               int kv_block_size, int num_blocks, hipStream_t stream);
+                               int kv_block_size, int kv_layout, int num_blocks,
+                               hipStream_t stream);
 
 /* Human-readable reason for this thread's last non-zero return ("" if none). */
 const char *mqa_last_error(void);

@@ -27,6 +27,8 @@ EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode",
             "mqa_topk_indices", "mqa_kcache_quantize_insert", "mqa_last_error")
 MQA_DTYPE_FP32 = 0
 MQA_DTYPE_BF16 = 1
+MQA_KV_SLOT_MAJOR = 0
+MQA_KV_PRESHUFFLED = 1
 
 
 class MQAError(RuntimeError):
@@ -63,11 +65,11 @@ def load_library(path: str = LIB_PATH):
     lib.mqa_logits_prefill.restype = I
     lib.mqa_logits_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.paged_mqa_logits_decode.restype = I
-    lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P]
+    lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, P]
     lib.mqa_topk_indices.restype = I
     lib.mqa_topk_indices.argtypes = [P, I, I, I, P, P]
     lib.mqa_kcache_quantize_insert.restype = I
-    lib.mqa_kcache_quantize_insert.argtypes = [P, I, P, P, I, I, I, I, P]
+    lib.mqa_kcache_quantize_insert.argtypes = [P, I, P, P, I, I, I, I, I, P]
     _lib = lib
     return lib
 
@@ -109,6 +111,10 @@ def _stream(stream, device) -> int:
     return int(getattr(stream, "cuda_stream", stream))
 
 
+def _layout(preshuffle: bool) -> int:
+    return MQA_KV_PRESHUFFLED if preshuffle else MQA_KV_SLOT_MAJOR
+
+
 def _tun(tunables: Optional[Tunables]):
     return ctypes.byref(tunables) if tunables is not None else None
 
@@ -145,10 +151,12 @@ def paged_mqa_logits_decode(q_fp8: torch.Tensor, kv_cache: torch.Tensor, weights
                             context_lens: torch.Tensor, block_tables: torch.Tensor,
                             max_model_len: int, kv_block_size: int = 64,
                             logits: Optional[torch.Tensor] = None, clean_logits: bool = True,
-                            tunables: Optional[Tunables] = None, stream=None) -> torch.Tensor:
+                            tunables: Optional[Tunables] = None, stream=None,
+                            preshuffle: bool = False) -> torch.Tensor:
     """q_fp8 [B,next_n,H,D] fp8, kv_cache [num_blocks, bs*(D+4)] bytes, weights
     [B*next_n,H] f32, context_lens [B] int32, block_tables [B,max_blocks] int32
-    -> logits [B*next_n, max_model_len] f32 (allocated if not given)."""
+    -> logits [B*next_n, max_model_len] f32 (allocated if not given).
+    preshuffle: the cache's K rows are in the preshuffled (16,16) order."""
     q = _bytes(q_fp8, "q_fp8")
     cache = _bytes(kv_cache, "kv_cache")
     B, next_n, H, D = q.shape
@@ -168,8 +176,8 @@ def paged_mqa_logits_decode(q_fp8: torch.Tensor, kv_cache: torch.Tensor, weights
         _dev(q, "q_fp8"), _dev(cache, "kv_cache"), _dev(weights, "weights", torch.float32),
         _dev(context_lens, "context_lens", torch.int32),
         _dev(block_tables, "block_tables", torch.int32), _dev(logits, "logits", torch.float32),
-        B, next_n, H, D, int(kv_block_size), num_blocks, block_tables.shape[1], int(max_model_len),
-        int(bool(clean_logits)), _tun(tunables), _stream(stream, q.device))
+        B, next_n, H, D, int(kv_block_size), _layout(preshuffle), num_blocks, block_tables.shape[1],
+        int(max_model_len), int(bool(clean_logits)), _tun(tunables), _stream(stream, q.device))
     _check(rc)
     return logits
 
@@ -193,9 +201,11 @@ def topk_indices(logits: torch.Tensor, k: int, indices: Optional[torch.Tensor] =
 
 
 def kcache_quantize_insert(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
-                           kv_block_size: int = 64, stream=None) -> torch.Tensor:
+                           kv_block_size: int = 64, stream=None,
+                           preshuffle: bool = False) -> torch.Tensor:
     """k [T, 128] float32 or bfloat16, slot_mapping [T] int64 (negative = skip),
-    kv_cache [num_blocks, kv_block_size * 132] uint8 (updated in place)."""
+    kv_cache [num_blocks, kv_block_size * 132] uint8 (updated in place; K rows
+    in the preshuffled (16,16) order when preshuffle is set)."""
     if k.dim() != 2:
         raise ValueError("k must be [num_tokens, head_dim]")
     T, D = k.shape
@@ -209,6 +219,6 @@ def kcache_quantize_insert(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache
         raise ValueError("slot_mapping must be [num_tokens]")
     rc = load_library().mqa_kcache_quantize_insert(
         _dev(k, "k"), dtype, _dev(slot_mapping, "slot_mapping", torch.int64), _dev(cache, "kv_cache"),
-        T, D, int(kv_block_size), cache.shape[0], _stream(stream, k.device))
+        T, D, int(kv_block_size), _layout(preshuffle), cache.shape[0], _stream(stream, k.device))
     _check(rc)
     return kv_cache

@@ -199,19 +199,25 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
                                        const float *weights, const int32_t *context_lens,
                                        const int32_t *block_tables, float *logits, int batch,
                                        int next_n, int num_heads, int head_dim, int kv_block_size,
-                                       int num_blocks, int max_blocks_per_seq, int max_model_len,
-                                       int clean_logits, const mqa_tunables *tun,
-                                       hipStream_t stream)
+                                       int kv_layout, int num_blocks, int max_blocks_per_seq,
+                                       int max_model_len, int clean_logits,
+                                       const mqa_tunables *tun, hipStream_t stream)
 {
     if (batch < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_model_len < 0)
         return fail(MQA_ERR_INVALID_ARG, "negative size argument");
     if (next_n < 1 || next_n > 8)
         return fail(MQA_ERR_INVALID_ARG, "next_n must be in 1..8 (got %d)", next_n);
+    if (kv_layout != MQA_KV_SLOT_MAJOR && kv_layout != MQA_KV_PRESHUFFLED)
+        return fail(MQA_ERR_INVALID_ARG, "kv_layout must be MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED "
+                    "(got %d)", kv_layout);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
                     "decode supports num_heads=32 with kv_block_size 1, 16, 64 or 128, or "
                     "num_heads 64 / 128 with kv_block_size 64; head_dim=128 (got %d, %d, %d)",
                     num_heads, head_dim, kv_block_size);
+    if (kv_layout == MQA_KV_PRESHUFFLED && kv_block_size < 16)
+        return fail(MQA_ERR_UNSUPPORTED, "the preshuffled layout needs kv_block_size 16, 64 or 128 "
+                    "(got %d)", kv_block_size);
     mqa_tunables t = {};
     if (tun)
         t = *tun;
@@ -268,6 +274,7 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     p.rows = rows;
     p.depth = t.ring_depth ? t.ring_depth : (any_depth ? 3 : 4);
     p.block_size = kv_block_size;
+    p.tiled = kv_layout == MQA_KV_PRESHUFFLED;
     const int64_t steps_max = ceil_div(max_model_len, 64);
     if (t.split_kv) {
         p.split_kv = t.split_kv;
@@ -318,7 +325,8 @@ extern "C" int mqa_topk_indices(const float *logits, int rows, int cols, int k, 
 
 extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
                                           uint8_t *kv_cache, int num_tokens, int head_dim,
-                                          int kv_block_size, int num_blocks, hipStream_t stream)
+                                          int kv_block_size, int kv_layout, int num_blocks,
+                                          hipStream_t stream)
 {
     if (num_tokens < 0 || num_blocks < 0)
         return fail(MQA_ERR_INVALID_ARG, "num_tokens=%d, num_blocks=%d must be >= 0", num_tokens,
@@ -331,6 +339,12 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
                     "K-cache insert supports head_dim=128, kv_block_size 1, 16, 64 or 128 "
                     "(got %d, %d)",
                     head_dim, kv_block_size);
+    if (kv_layout != MQA_KV_SLOT_MAJOR && kv_layout != MQA_KV_PRESHUFFLED)
+        return fail(MQA_ERR_INVALID_ARG, "kv_layout must be MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED "
+                    "(got %d)", kv_layout);
+    if (kv_layout == MQA_KV_PRESHUFFLED && kv_block_size < 16)
+        return fail(MQA_ERR_UNSUPPORTED, "the preshuffled layout needs kv_block_size 16, 64 or 128 "
+                    "(got %d)", kv_block_size);
     if (num_tokens == 0)
         return ok();
     if (!k || !slot_mapping || !kv_cache)
@@ -347,6 +361,7 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
     p.block_size = kv_block_size;
     p.num_slots = (int64_t)num_blocks * kv_block_size;
     p.bf16 = k_dtype == MQA_DTYPE_BF16;
+    p.tiled = kv_layout == MQA_KV_PRESHUFFLED;
     if (trace_on())
         std::fprintf(stderr, "[mqa] kcache insert tokens=%d dtype=%d\n", num_tokens, k_dtype);
     hipError_t e = mqa::launch_kcache_insert(p, stream);

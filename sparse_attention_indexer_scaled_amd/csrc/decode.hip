@@ -49,6 +49,7 @@ struct DecodeArgs {
     int clean;
     int groups;
     int split;
+    int tiled;  // K rows of a block in the preshuffled (16,16) order
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -74,6 +75,15 @@ constexpr int kStreamHint = 2;
 // Blocks of 16 or more tokens hold whole 8-token chunks, so each chunk is one
 // coalesced 1 KiB read; the step's table entries (64 / BS of them, or one
 // entry covering several steps) are read with scalar loads.
+//
+// Such blocks may also hold their K rows in the preshuffled (16,16) order
+// (the 64-token pairing on the aiter PR 5047 page, "Technical Details"): the
+// slots in groups of 16, each group storing 16-byte granule u of its 16 rows
+// (row by row) before granule u + 1, so granule u of block row r sits at
+// (r / 16) 2048 + 256 u + 16 (r % 16).  Only the source addresses change: a
+// chunk's 64 granules are then eight 128-byte runs, and the two chunks of a
+// 16-row group read one contiguous 2 KiB; the ring slot is filled exactly as
+// from a slot-major block.
 // The block pointers of one step (one per table entry the step touches).
 template <int N>
 struct StepBlocks {
@@ -121,7 +131,7 @@ struct Gather {
 // pointers stay in registers).
 template <int G, int BS>
 __device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_per_step(BS)> blk_of,
-                                             int off, int g, int lane)
+                                             int off, bool tiled, int g, int lane)
 {
     constexpr int kEntries = entries_per_step(BS);
     constexpr int KC = kChunks - 1;
@@ -138,8 +148,10 @@ __device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_pe
                 if (e == i)
                     blk = blk_of.p[i];
             const int row = (BS >= kStep ? off + 8 * c : (8 * c) % BS) + (q & 7);
-            __builtin_amdgcn_global_load_lds(blk + row * kDim + (q >> 3) * 16,
-                                             slot + 1024 * c, 16, 0, kStreamHint);
+            const int u = q >> 3;
+            const int src = tiled ? (row >> 4) * (16 * kDim) + u * 256 + (row & 15) * 16
+                                  : row * kDim + u * 16;
+            __builtin_amdgcn_global_load_lds(blk + src, slot + 1024 * c, 16, 0, kStreamHint);
         }
     }
     if (G == 1 || g == G - 1) {
@@ -362,6 +374,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         };
 
         const int32_t *table = tables + (int64_t)b * a.mbps;
+        const bool tiled = a.tiled != 0;
         lds_u8 *ring = (lds_u8 *)ring_mem;
         const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
         using Gth = Gather<(BS == 1 ? kBlock : BS)>;  // unused for BS = 1
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
             for (int i = 0; i < D - 1; ++i)
                 if (st0 + i < st1) {
                     const typename Gth::Src src = Gth::fetch(cache, table, st0 + i, last_entry);
-                    request_step<G, BS>(ring + i * kSlotBytes, src.blk, src.off, g, lane);
+                    request_step<G, BS>(ring + i * kSlotBytes, src.blk, src.off, tiled, g, lane);
                 }
         }
         // Between requesting block k and waiting for it a wave requests the
@@ -437,7 +450,8 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                                       cache, g, lane);
             } else {
                 if (st + D - 1 < st1)
-                    request_step<G, BS>(ring + wr * kSlotBytes, next.blk, next.off, g, lane);
+                    request_step<G, BS>(ring + wr * kSlotBytes, next.blk, next.off, tiled, g,
+                                        lane);
                 next = Gth::fetch(cache, table, min(st + D, st1 - 1), last_entry);
             }
             KStep kb;
@@ -508,6 +522,7 @@ hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream)
     a.clean = p.clean;
     a.groups = (p.next_n + p.rows - 1) / p.rows;
     a.split = p.split_kv;
+    a.tiled = p.tiled;
     const int grid = p.batch * a.split;
     if (p.head_tiles == 2) {
         // 64 heads: at most 2 rows per wave (Q and weights take 64 VGPRs a row)

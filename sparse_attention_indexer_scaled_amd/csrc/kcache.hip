@@ -9,8 +9,10 @@
 //   q     = e4m3fn_rne(clamp(k / scale, -448, 448))
 // then the 128 code bytes go to the token's slot (one 128-byte row per wave,
 // 2-byte stores) and lane 0 writes the scale, in the block-split layout of
-// the decode cache.  Tokens whose slot is negative or past the cache are
-// skipped.  K must be finite.
+// the decode cache: K rows slot-major, or in the preshuffled (16,16) order
+// (byte d of slot s at (s/16) 2048 + (d/16) 256 + (s%16) 16 + d%16; the
+// 64-token pairing on the aiter PR 5047 page, "Technical Details").  Tokens
+// whose slot is negative or past the cache are skipped.  K must be finite.
 #include "device.h"
 #include "launch.h"
 
@@ -48,7 +50,7 @@ __device__ __forceinline__ uint32_t e4m3fn_rne(float q)
 template <bool BF16>
 __global__ __launch_bounds__(64 * kTokensPerBlock) void kcache_insert_kernel(
     const void *__restrict__ k, const int64_t *__restrict__ slots, uint8_t *__restrict__ cache,
-    int tokens, int block_size, int64_t num_slots)
+    int tokens, int block_size, int64_t num_slots, int tiled)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kTokensPerBlock + (int)(threadIdx.x >> 6);
@@ -78,7 +80,10 @@ __global__ __launch_bounds__(64 * kTokensPerBlock) void kcache_insert_kernel(
     const int64_t blk = s / block_size;
     const int slot = (int)(s - blk * block_size);
     uint8_t *base = cache + blk * (int64_t)block_size * (kDim + 4);
-    *reinterpret_cast<uint16_t *>(base + (int64_t)slot * kDim + 2 * lane) = (uint16_t)c;
+    const int d = 2 * lane;
+    const int off = tiled ? (slot >> 4) * (16 * kDim) + (d >> 4) * 256 + (slot & 15) * 16 + (d & 15)
+                          : slot * kDim + d;
+    *reinterpret_cast<uint16_t *>(base + off) = (uint16_t)c;
     if (lane == 0)
         *reinterpret_cast<float *>(base + (int64_t)block_size * kDim + 4 * slot) = scale;
 }
@@ -90,10 +95,10 @@ hipError_t launch_kcache_insert(const KcacheLaunch &p, hipStream_t stream)
     const int grid = (p.tokens + kTokensPerBlock - 1) / kTokensPerBlock;
     if (p.bf16)
         hipLaunchKernelGGL(kcache_insert_kernel<true>, dim3(grid), dim3(64 * kTokensPerBlock), 0,
-                           stream, p.k, p.slots, p.cache, p.tokens, p.block_size, p.num_slots);
+                           stream, p.k, p.slots, p.cache, p.tokens, p.block_size, p.num_slots, p.tiled);
     else
         hipLaunchKernelGGL(kcache_insert_kernel<false>, dim3(grid), dim3(64 * kTokensPerBlock), 0,
-                           stream, p.k, p.slots, p.cache, p.tokens, p.block_size, p.num_slots);
+                           stream, p.k, p.slots, p.cache, p.tokens, p.block_size, p.num_slots, p.tiled);
     return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@ struct DecodeLaunch {
                    // 4 for block sizes other than 64
     int block_size;  // tokens per cache block: 1, 16, 64 or 128
     int head_tiles;  // num_heads / 32: 1, 2 or 4 (2 and 4: block size 64, depth 4)
+    int tiled;       // 1: K rows in the preshuffled (16,16) order (block size >= 16)
 };
 
 // Largest k of the row-wise top-k.
@@ -64,6 +65,7 @@ struct KcacheLaunch {
     int block_size;
     int64_t num_slots;    // num_blocks * block_size
     int bf16;
+    int tiled;            // 1: K rows in the preshuffled (16,16) order
 };
 
 // Bytes of LDS a decode workgroup uses for a ring of `depth` blocks.

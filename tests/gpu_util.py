@@ -68,7 +68,7 @@ def run_decode(d, clean=True, tun=None, fill=float("nan"), dv=None):
     out = torch.full((rows, d.max_model_len), fill, dtype=torch.float32, device="cuda")
     _native.paged_mqa_logits_decode(dv["q"], dv["cache"], dv["w"], dv["ctx"], dv["bt"],
                                     d.max_model_len, d.block_size, logits=out,
-                                    clean_logits=clean, tunables=tun)
+                                    clean_logits=clean, tunables=tun, preshuffle=d.preshuffle)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

@@ -59,7 +59,8 @@ def test_tunables_struct_matches_header():
 def test_error_codes_match_header():
     text = open(HEADER).read()
     for name in ("MQA_OK", "MQA_ERR_INVALID_ARG", "MQA_ERR_UNSUPPORTED", "MQA_ERR_LAUNCH",
-                 "MQA_ERR_DEVICE"):
+                 "MQA_ERR_DEVICE", "MQA_DTYPE_FP32", "MQA_DTYPE_BF16", "MQA_KV_SLOT_MAJOR",
+                 "MQA_KV_PRESHUFFLED"):
         m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert int(m.group(1)) == getattr(_native, name), name
 
@@ -77,8 +78,8 @@ def _prefill(lib, ptrs, M=4, N=8, H=32, D=128, clean=1, tun=None):
     return lib.mqa_logits_prefill(*ptrs, M, N, H, D, clean, tun, None)
 
 
-def _decode(lib, ptrs, B=2, nn=1, H=32, D=128, bs=64, nb=4, mbps=2, mml=128, tun=None):
-    return lib.paged_mqa_logits_decode(*ptrs, B, nn, H, D, bs, nb, mbps, mml, 1, tun, None)
+def _decode(lib, ptrs, B=2, nn=1, H=32, D=128, bs=64, nb=4, mbps=2, mml=128, tun=None, layout=0):
+    return lib.paged_mqa_logits_decode(*ptrs, B, nn, H, D, bs, layout, nb, mbps, mml, 1, tun, None)
 
 
 def test_prefill_validation(lib):
@@ -121,6 +122,12 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls, H=64, bs=16) == mqa._native.MQA_ERR_UNSUPPORTED
     bad = _native.Tunables(rows_per_block=2)  # 128 heads: one row per wave
     assert _decode(lib, nulls, H=128, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    assert _decode(lib, nulls, layout=2) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "kv_layout" in mqa.last_error()
+    assert _decode(lib, nulls, bs=1, layout=1) == mqa._native.MQA_ERR_UNSUPPORTED
+    for bs in (16, 64, 128):
+        assert _decode(lib, nulls, bs=bs, layout=1) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
+        assert "NULL" in mqa.last_error()
     assert _decode(lib, nulls, B=0) == 0
     assert _decode(lib, nulls, mml=0) == 0
     assert _decode(lib, nulls) == mqa._native.MQA_ERR_INVALID_ARG
@@ -149,14 +156,18 @@ def test_topk_validation(lib):
 
 def test_kcache_validation(lib):
     f = lib.mqa_kcache_quantize_insert
-    assert f(None, 0, None, None, -1, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
-    assert f(None, 2, None, None, 5, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 0, None, None, -1, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 2, None, None, 5, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert "k_dtype" in mqa.last_error()
-    assert f(None, 0, None, None, 5, 64, 64, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert f(None, 1, None, None, 5, 128, 32, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert f(None, 0, None, None, 0, 128, 64, 4, None) == 0
-    assert f(None, 0, None, None, 5, 128, 64, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
-    assert f(P(0x1004), 0, P(0x2000), P(0x3000), 5, 128, 64, 4, None) == \
+    assert f(None, 0, None, None, 5, 64, 64, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 1, None, None, 5, 128, 32, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 5, 128, 64, 3, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "kv_layout" in mqa.last_error()
+    assert f(None, 0, None, None, 5, 128, 1, 1, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 0, 128, 64, 0, 4, None) == 0
+    assert f(None, 0, None, None, 5, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(None, 0, None, None, 5, 128, 64, 1, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
+    assert f(P(0x1004), 0, P(0x2000), P(0x3000), 5, 128, 64, 0, 4, None) == \
         mqa._native.MQA_ERR_INVALID_ARG
     assert "aligned" in mqa.last_error()
 

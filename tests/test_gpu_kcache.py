@@ -25,12 +25,13 @@ def _gpu():
     lib()
 
 
-def gpu_insert(c):
+def gpu_insert(c, preshuffle=False):
     cache = dev(c.kv_cache)
     k = dev(c.k)
     if c.bf16:
         k = k.to(torch.bfloat16)
-    _native.kcache_quantize_insert(k, dev(c.slot_mapping), cache, kv_block_size=c.block_size)
+    _native.kcache_quantize_insert(k, dev(c.slot_mapping), cache, kv_block_size=c.block_size,
+                                   preshuffle=preshuffle)
     torch.cuda.synchronize()
     return cache.cpu().numpy()
 
@@ -54,6 +55,19 @@ def test_insert_other_block_sizes(bs):
     got = gpu_insert(c)
     want = oracle_kcache.insert(c.kv_cache, c.k, c.slot_mapping, bs)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("bs", [16, 64, 128])
+def test_insert_preshuffled_layout(bs, bf16):
+    c = inputs.make_kcache_insert(900, -(-900 // bs) + 2, seed=640 + bs + bf16, block_size=bs,
+                                  bf16=bf16)
+    say("kcache insert preshuffled bs=%d bf16=%d" % (bs, bf16))
+    got = gpu_insert(c, preshuffle=True)
+    want = oracle_kcache.insert(c.kv_cache, c.k, c.slot_mapping, bs, preshuffle=True)
+    if not np.array_equal(got, want):
+        diff = np.argwhere(got != want)
+        raise AssertionError("%d bytes differ, first at %s" % (len(diff), diff[0].tolist()))
 
 
 def test_rounding_boundaries_on_gpu():
@@ -96,6 +110,25 @@ def test_insert_then_decode_end_to_end():
     out = run_decode(dataclasses.replace(d, kv_cache=gpu_cache))
     ref, mag, _ = oracle_decode(dataclasses.replace(d, kv_cache=oracle_cache))
     assert_parity(out, ref, mag, "decode after insert")
+
+
+def test_preshuffled_insert_then_decode_end_to_end():
+    """The same chain in the preshuffled (16,16) layout, 16-token blocks."""
+    import dataclasses
+    d = inputs.make_decode(2, 2, [333, 1000], 1024, seed=612, block_size=16, preshuffle=True)
+    rng = np.random.default_rng(613)
+    slots = np.concatenate([d.block_tables[b, np.arange(int(d.context_lens[b])) // 16] * 16
+                            + np.arange(int(d.context_lens[b])) % 16 for b in range(d.B)])
+    k = (rng.standard_normal((slots.size, 128)) * 2).astype(np.float32)
+    empty = np.zeros_like(d.kv_cache)
+    say("kcache insert (preshuffled) feeding decode")
+    c = inputs.KcacheInsertInputs(k, slots.astype(np.int64), empty, 16, False)
+    gpu_cache = gpu_insert(c, preshuffle=True)
+    oracle_cache = oracle_kcache.insert(empty, k, slots, 16, preshuffle=True)
+    assert np.array_equal(gpu_cache, oracle_cache)
+    out = run_decode(dataclasses.replace(d, kv_cache=gpu_cache))
+    ref, mag, _ = oracle_decode(dataclasses.replace(d, kv_cache=oracle_cache))
+    assert_parity(out, ref, mag, "preshuffled decode after insert")
 
 
 def test_zero_tokens_is_a_no_op():

@@ -206,6 +206,41 @@ def test_block_size_does_not_change_bits(bs):
     assert np.array_equal(run_decode(d64), run_decode(d), equal_nan=True)
 
 
+@pytest.mark.parametrize("bs", [16, 64, 128])
+@pytest.mark.parametrize("B,next_n,ctx,mml", BLOCK_SIZE_CASES,
+                         ids=[f"B{b}-nn{n}-mml{m}" for b, n, _, m in BLOCK_SIZE_CASES])
+def test_decode_preshuffled_layout(bs, B, next_n, ctx, mml):
+    """Blocks whose K rows are in the preshuffled (16,16) order, against the
+    oracle's own reading of that order; ragged, short and empty contexts,
+    NaN-poisoned unused slots."""
+    d = inputs.make_decode(B, next_n, ctx, mml, seed=350 + bs + mml, block_size=bs, poison=True,
+                           preshuffle=True)
+    say("decode preshuffled bs=%d B=%d next_n=%d ctx=%s mml=%d" % (bs, B, next_n, ctx, mml))
+    ref, mag, _ = oracle_decode(d)
+    tuns = [None, Tunables(split_kv=3), Tunables(rows_per_block=1, split_kv=1)]
+    if bs == 64:
+        tuns += [Tunables(ring_depth=2), Tunables(ring_depth=6, split_kv=2)]
+    for tun in tuns:
+        out = run_decode(d, tun=tun)
+        assert_parity(out, ref, mag, f"decode_preshuffled_bs{bs}_B{B}_nn{next_n}")
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+@pytest.mark.parametrize("bs", [16, 64, 128])
+def test_preshuffled_layout_does_not_change_bits(bs, H):
+    """The same draws stored slot-major and preshuffled give the same output
+    bit for bit: the layout changes only where the loads read from."""
+    if H != 32 and bs != 64:
+        pytest.skip("64 and 128 heads use 64-token blocks only")
+    kw = dict(B=3, next_n=4, context_lens=[900, 64, 2500], max_model_len=2560, seed=341, H=H,
+              block_size=bs)
+    plain = inputs.make_decode(**kw)
+    tiled = inputs.make_decode(preshuffle=True, **kw)
+    say("decode preshuffled vs slot-major bs=%d H=%d" % (bs, H))
+    assert not np.array_equal(plain.kv_cache, tiled.kv_cache)
+    assert np.array_equal(run_decode(plain), run_decode(tiled), equal_nan=True)
+
+
 # ---------------------------------------------------------------------------
 # GPU self-invariants (bitwise)
 # ---------------------------------------------------------------------------
