@@ -104,7 +104,7 @@ class Workload:
             base = dict(q=dev(host.q), k=dev(host.k), sc=dev(host.kv_scale), w=dev(host.weights),
                         ks=dev(host.ks), ke=dev(host.ke))
             self.out_shape = (host.M, host.N)
-            self.bytes = workload.prefill_essential_bytes(host.M, host.N, H=host.H)
+            self.bytes = workload.prefill_essential_bytes(host.M, host.N, H=host.H, D=host.D)
             self.pairs = workload.prefill_valid_pairs(host.ks, host.ke, host.N)
             set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + host.M * host.N * 4
         else:
@@ -118,7 +118,7 @@ class Workload:
                                                      host.max_model_len)
             set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
                 self.out_shape[0] * self.out_shape[1] * 4
-        self.flops = self.pairs * workload.flops_per_pair(H=host.H)
+        self.flops = self.pairs * workload.flops_per_pair(H=host.H, D=host.D)
         nsets = 1 if hot else min(64, max(1, -(-COLD_BYTES // set_bytes)))
         self.sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
         self.outs = [torch.empty(self.out_shape, dtype=torch.float32, device="cuda")
@@ -541,7 +541,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15) if i != args.workload]
     results, head = {}, None
     for idx in order:
         wl = make_workload(idx, args.hot, tun)

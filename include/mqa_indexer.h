@@ -79,11 +79,12 @@ typedef struct mqa_tunables {
 /*
  * Support gate (both pages, "Technical Details": callers ask before routing a
  * shape to these kernels and go elsewhere instead of failing).  Supported:
- * head_dim 128 with num_heads 32, 64 or 128 (the head counts the issue page
- * about next_n tiling sweeps).  kv_block_size: 0 asks about prefill; 1, 16,
- * 64 or 128 about paged decode with blocks of that many tokens (64 only with
- * 64 or 128 heads).  Returns 1 if the current HIP device is gfx950
- * and the shape is supported, else 0.  Never fails.
+ * num_heads 32, 64 or 128 (the head counts the issue page about next_n tiling
+ * sweeps) with head_dim 128, and for prefill also head_dim 64 (the head dims
+ * of the aiter PR 5046 page's test sweep, "Test Plan").  kv_block_size: 0 asks
+ * about prefill; 1, 16, 64 or 128 about paged decode with blocks of that many
+ * tokens (64 only with 64 or 128 heads).  Returns 1 if the current HIP device
+ * is gfx950 and the shape is supported, else 0.  Never fails.
  */
 int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
 
@@ -91,7 +92,7 @@ int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
  * Prefill logits over a contiguous, already-gathered K (aiter PR 5046 page,
  * "Motivation" and "Technical Details").
  *
- *   q_fp8        [M, num_heads, head_dim]  fp8 e4m3fn
+ *   q_fp8        [M, num_heads, head_dim]  fp8 e4m3fn (head_dim 64 or 128)
  *   k_fp8        [N, head_dim]             fp8 e4m3fn
  *   kv_scale     [N]                       fp32, >= 0
  *   weights      [M, num_heads]            fp32

@@ -78,12 +78,15 @@ int check_device()
     return MQA_OK;
 }
 
-// 32, 64 or 128 index heads (the pages sweep all three); head dim 128; cache
-// blocks of 1, 16, 64 or 128 tokens for decode (0 asks about prefill), 64 only
-// with more than 32 heads.
+// 32, 64 or 128 index heads (the pages sweep all three); head dim 128, or 64
+// for prefill (the prefill page's test sweep covers head dims 64 and 128, the
+// decode page's only 128); cache blocks of 1, 16, 64 or 128 tokens for decode
+// (0 asks about prefill), 64 only with more than 32 heads.
 bool shape_supported(int num_heads, int head_dim, int kv_block_size)
 {
-    if (head_dim != 128 || (num_heads != 32 && num_heads != 64 && num_heads != 128))
+    if (num_heads != 32 && num_heads != 64 && num_heads != 128)
+        return false;
+    if (head_dim != 128 && !(head_dim == 64 && kv_block_size == 0))
         return false;
     if (num_heads != 32)
         return kv_block_size == 0 || kv_block_size == 64;
@@ -124,7 +127,7 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
         return fail(MQA_ERR_INVALID_ARG, "M=%d, N=%d must be >= 0", M, N);
     if (!shape_supported(num_heads, head_dim, 0))
         return fail(MQA_ERR_UNSUPPORTED,
-                    "prefill supports num_heads 32, 64 or 128 and head_dim 128 (got %d, %d)",
+                    "prefill supports num_heads 32, 64 or 128 and head_dim 64 or 128 (got %d, %d)",
                     num_heads, head_dim);
     const int head_tiles = num_heads / 32;
     const int max_block_m = 8 / head_tiles;  // Q and weights of a wave's rows stay in VGPRs
@@ -171,6 +174,7 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     // steps.  High-m first for long causal chunks (aiter PR 5046 page,
     // "Technical Details": N > 2048).
     p.head_tiles = head_tiles;
+    p.head_dim = head_dim;
     p.block_m = t.block_m ? t.block_m : std::min(M >= 1024 ? 8 : 4, max_block_m);
     p.num_warps = t.num_warps ? t.num_warps : (M >= 1024 ? 1 : 4);
     const int64_t nrb = ceil_div(M, p.block_m);

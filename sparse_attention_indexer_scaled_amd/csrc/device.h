@@ -1,15 +1,15 @@
 // Device building blocks shared by the prefill and decode kernels (gfx950).
 //
 // One wave (64 lanes) computes the scores of one query row against a 32-token
-// K tile with two fp8 MFMAs, v_mfma_f32_32x32x64_f8f6f4: A = the row's Q
-// (32 heads x 128 dims), B = K^T (128 dims x 32 tokens), D = S[head][token] in
-// fp32.  The contraction is a dense 32-head x token matrix product, which is
-// why it runs on the matrix cores (both pages, "Technical Details": 32 heads x
-// 32 tokens per fp8 MFMA tile).
+// K tile with fp8 MFMAs, v_mfma_f32_32x32x64_f8f6f4 (two at head dim 128, one
+// at head dim 64): A = the row's Q (32 heads x D dims), B = K^T (D dims x 32
+// tokens), D = S[head][token] in fp32.  The contraction is a dense 32-head x
+// token matrix product, which is why it runs on the matrix cores (both pages,
+// "Technical Details": 32 heads x 32 tokens per fp8 MFMA tile).
 //
 // Operand placement.  Lane l = 32 g + t (t = l & 31, g = l >> 5) holds, for row
-// t of its operand (a head of Q, a token of K), the four 16-byte chunks at
-// bytes (2j + g) * 16, j = 0..3.  Chunks j = 0, 1 feed the first MFMA (dims
+// t of its operand (a head of Q, a token of K), the 16-byte chunks at bytes
+// (2j + g) * 16, j = 0..D/32-1.  Chunks j = 0, 1 feed the first MFMA (dims
 // 0..63), chunks 2, 3 the second (dims 64..127).  The MFMA pairs A's byte slot
 // (lane group, byte) with B's identical slot, so any placement that Q and K
 // share computes the full dot product; this one lets lanes t and t + 32 read
@@ -38,10 +38,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// 64 fp8 bytes per lane of one 32-row x 128-dim operand (a K tile or a Q row).
-struct Frag {
-    i32x4 c[4];
+// D/2 fp8 bytes per lane of one 32-row x D-dim operand (a K tile or a Q row).
+template <int D>
+struct Operand {
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    i32x4 c[D / 32];
 };
+using Frag = Operand<kDim>;
 
 // The 16 head weights matching this lane's accumulator registers.
 struct Weights16 {
@@ -51,20 +54,13 @@ struct Weights16 {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Row `rowptr` is this lane's own row (head or token) of the operand.
-__device__ __forceinline__ void load_frag(Frag &f, const uint8_t *rowptr, int lane)
+template <int D>
+__device__ __forceinline__ void load_frag(Operand<D> &f, const uint8_t *rowptr, int lane)
 {
     const uint8_t *p = rowptr + (lane >> 5) * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < D / 32; ++j)
         f.c[j] = *reinterpret_cast<const i32x4 *>(p + 32 * j);
-}
-
-__device__ __forceinline__ void load_frag_nt(Frag &f, const uint8_t *rowptr, int lane)
-{
-    const uint8_t *p = rowptr + (lane >> 5) * 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        f.c[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p + 32 * j));
 }
 
 // wrow: the 32 fp32 weights of one query row.  Register r of the accumulator
@@ -87,11 +83,13 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b
 }
 
 // S[head][token] for one query row and one 32-token tile.
-__device__ __forceinline__ f32x16 row_scores(const Frag &q, const Frag &k)
+template <int D>
+__device__ __forceinline__ f32x16 row_scores(const Operand<D> &q, const Operand<D> &k)
 {
     f32x16 acc = {};
-    acc = mfma_fp8(q.c[0], q.c[1], k.c[0], k.c[1], acc);
-    acc = mfma_fp8(q.c[2], q.c[3], k.c[2], k.c[3], acc);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j)
+        acc = mfma_fp8(q.c[2 * j], q.c[2 * j + 1], k.c[2 * j], k.c[2 * j + 1], acc);
     return acc;
 }
 
@@ -123,10 +121,12 @@ __device__ __forceinline__ float pair_head_sum(float a, float b)
 
 // One 64-token step of K in the MFMA operand layout: two 32-token tiles and
 // the tokens' scales (lane t of tile h holds the scale of token 32 h + t).
-struct KStep {
-    Frag t[2];
+template <int D>
+struct KStepOf {
+    Operand<D> t[2];
     float sc[2];
 };
+using KStep = KStepOf<kDim>;
 
 // Scores, relu.weight sums and kv-scaled head sums for one 64-token step and
 // R query rows of 32 HT heads each (q[r][ht], w[r][ht]: head tile ht of row r).
@@ -135,8 +135,8 @@ struct KStep {
 // MFMAs of item i+1 are issued before the relu.weight epilogue of item i, so
 // the epilogue never waits on the MFMA it consumes.  A row's head tiles are
 // summed in order; with one head tile the sum is the item itself.
-template <int R, int HT>
-__device__ __forceinline__ void step_scores(const KStep &k, const Frag (&q)[R][HT],
+template <int R, int HT, int D = kDim>
+__device__ __forceinline__ void step_scores(const KStepOf<D> &k, const Operand<D> (&q)[R][HT],
                                             const Weights16 (&w)[R][HT],
                                             float (&tot)[2][(R + 1) / 2])
 {

@@ -23,6 +23,7 @@ struct PrefillLaunch {
     int num_warps; // waves per workgroup
     int reverse;   // 1: high-m row blocks first
     int head_tiles;  // num_heads / 32: 1, 2 or 4
+    int head_dim;    // 64 or 128
 };
 
 struct DecodeLaunch {

@@ -14,7 +14,7 @@
 // each wave keeps its own independent K stream in flight).  Each wave keeps
 // its BM rows' Q and weights in VGPRs and, per step, loads 64 K rows + scales
 // straight into VGPRs (no LDS; the whole K buffer is shared by every row block
-// and stays L2/MALL resident), runs 2 fp8 MFMAs per (row, 32-token tile), the
+// and stays L2/MALL resident), runs D/64 fp8 MFMAs per (row, 32-token tile), the
 // in-lane relu.weight sum, one permlane32 swap + add per row pair, the
 // once-per-column kv_scale multiply, and a masked store.  With clean_logits the
 // same waves write -inf left and right of the column range.
@@ -42,19 +42,20 @@ struct PrefillArgs {
 
 // Step starting at column n0.  Rows past N are clamped to N - 1: the load stays
 // in bounds and the column is never stored.
-__device__ __forceinline__ void load_kstep(KStep &k, const uint8_t *kbuf, const float *scale,
+template <int D>
+__device__ __forceinline__ void load_kstep(KStepOf<D> &k, const uint8_t *kbuf, const float *scale,
                                            int64_t n0, int N, int lane)
 {
     const int t = lane & 31;
     const int64_t n_a = min(n0 + t, (int64_t)N - 1);
     const int64_t n_b = min(n0 + kTile + t, (int64_t)N - 1);
-    load_frag(k.t[0], kbuf + n_a * kDim, lane);
-    load_frag(k.t[1], kbuf + n_b * kDim, lane);
+    load_frag(k.t[0], kbuf + n_a * D, lane);
+    load_frag(k.t[1], kbuf + n_b * D, lane);
     k.sc[0] = scale[n_a];
     k.sc[1] = scale[n_b];
 }
 
-template <int BM, int HT>
+template <int BM, int HT, int D>
 __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict__ qbuf,
                                                       const uint8_t *__restrict__ kbuf,
                                                       const float *__restrict__ scale,
@@ -118,14 +119,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
     int st = st0 + wave;
     if (st < st1) {
         constexpr int H = kHeads * HT;
-        Frag q[BM][HT];
+        Operand<D> q[BM][HT];
         Weights16 w[BM][HT];
 #pragma unroll
         for (int r = 0; r < BM; ++r) {
             const int64_t row = m0 + min(r, nrows - 1);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                load_frag(q[r][ht], qbuf + row * (H * kDim) + (ht * kHeads + t) * kDim, lane);
+                load_frag(q[r][ht], qbuf + row * (H * D) + (ht * kHeads + t) * D, lane);
                 load_weights(w[r][ht], wbuf + row * H + ht * kHeads, lane);
             }
         }
@@ -145,20 +146,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
         // Two step buffers used alternately; each half issues the next
         // step's loads before waiting for the current one (the
         // sched_barrier keeps the compiler from hoisting the wait above them).
-        KStep A, B;
+        KStepOf<D> A, B;
         load_kstep(A, kbuf, scale, (int64_t)st * kStep, N, lane);
         while (true) {
             load_kstep(B, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
             __builtin_amdgcn_sched_barrier(0);
             float tot[2][NP];
-            step_scores<BM, HT>(A, q, w, tot);
+            step_scores<BM, HT, D>(A, q, w, tot);
             store_step(st, tot);
             st += nw;
             if (st >= st1)
                 break;
             load_kstep(A, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
             __builtin_amdgcn_sched_barrier(0);
-            step_scores<BM, HT>(B, q, w, tot);
+            step_scores<BM, HT, D>(B, q, w, tot);
             store_step(st, tot);
             st += nw;
             if (st >= st1)
@@ -177,13 +178,41 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
     }
 }
 
-template <int BM, int HT = 1>
+template <int BM, int HT, int D>
 hipError_t launch_bm(const PrefillLaunch &p, const PrefillArgs &a, int grid, int block,
                      hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill_kernel<BM, HT>), dim3(grid), dim3(block), 0, stream, p.q, p.k,
+    hipLaunchKernelGGL((prefill_kernel<BM, HT, D>), dim3(grid), dim3(block), 0, stream, p.q, p.k,
                        p.kv_scale, p.weights, p.ks, p.ke, p.logits, a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dim(const PrefillLaunch &p, const PrefillArgs &a, int grid, int block,
+                      hipStream_t stream)
+{
+    if (p.head_tiles == 2) {  // 64 heads: at most 4 rows per wave
+        switch (p.block_m) {
+        case 1: return launch_bm<1, 2, D>(p, a, grid, block, stream);
+        case 2: return launch_bm<2, 2, D>(p, a, grid, block, stream);
+        case 4: return launch_bm<4, 2, D>(p, a, grid, block, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (p.head_tiles == 4) {  // 128 heads: at most 2 rows per wave
+        switch (p.block_m) {
+        case 1: return launch_bm<1, 4, D>(p, a, grid, block, stream);
+        case 2: return launch_bm<2, 4, D>(p, a, grid, block, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (p.block_m) {
+    case 1: return launch_bm<1, 1, D>(p, a, grid, block, stream);
+    case 2: return launch_bm<2, 1, D>(p, a, grid, block, stream);
+    case 4: return launch_bm<4, 1, D>(p, a, grid, block, stream);
+    case 8: return launch_bm<8, 1, D>(p, a, grid, block, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 } // namespace
@@ -199,26 +228,9 @@ hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream)
     a.reverse = p.reverse;
     const int grid = a.nrb * a.split;
     const int block = 64 * p.num_warps;
-    if (p.head_tiles == 2) {  // 64 heads: at most 4 rows per wave
-        switch (p.block_m) {
-        case 1: return launch_bm<1, 2>(p, a, grid, block, stream);
-        case 2: return launch_bm<2, 2>(p, a, grid, block, stream);
-        case 4: return launch_bm<4, 2>(p, a, grid, block, stream);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    if (p.head_tiles == 4) {  // 128 heads: at most 2 rows per wave
-        switch (p.block_m) {
-        case 1: return launch_bm<1, 4>(p, a, grid, block, stream);
-        case 2: return launch_bm<2, 4>(p, a, grid, block, stream);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    switch (p.block_m) {
-    case 1: return launch_bm<1>(p, a, grid, block, stream);
-    case 2: return launch_bm<2>(p, a, grid, block, stream);
-    case 4: return launch_bm<4>(p, a, grid, block, stream);
-    case 8: return launch_bm<8>(p, a, grid, block, stream);
+    switch (p.head_dim) {
+    case 64: return launch_dim<64>(p, a, grid, block, stream);
+    case 128: return launch_dim<128>(p, a, grid, block, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -329,6 +329,8 @@ CONFIGS = {
     # the headline decode shape in the preshuffled (16,16) 64-token cache
     14: dict(kind="decode", name="decode_B16_nn6_ctx131072_preshuffle", B=16, next_n=6,
              ctx=131072, mml=131072, preshuffle=True),
+    # the long prefill chunk at head dim 64
+    15: dict(kind="prefill", name="prefill_M4096_N32768_d64", M=4096, N=32768, D=64),
 }
 
 
@@ -337,7 +339,7 @@ def make_config(idx: int, poison: bool = False):
     c = CONFIGS[idx]
     seed = 1000 + idx
     if c["kind"] == "prefill":
-        return make_prefill(c["M"], c["N"], seed, H=c.get("H", HEADS))
+        return make_prefill(c["M"], c["N"], seed, H=c.get("H", HEADS), D=c.get("D", HEAD_DIM))
     return make_decode(c["B"], c["next_n"], c["ctx"], c["mml"], seed,
                        ctx_range=c.get("ctx_range"), poison=poison,
                        block_size=c.get("block_size", KV_BLOCK), H=c.get("H", HEADS),

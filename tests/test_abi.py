@@ -66,8 +66,8 @@ def test_error_codes_match_header():
 
 
 def test_gate_rejects_other_shapes(lib):
-    for h, d, bs in [(48, 128, 0), (32, 64, 0), (64, 128, 16), (32, 128, 32), (32, 128, 2),
-                     (256, 128, 64)]:
+    for h, d, bs in [(48, 128, 0), (32, 96, 0), (32, 64, 64), (64, 64, 64), (32, 64, 16),
+                     (64, 128, 16), (32, 128, 32), (32, 128, 2), (256, 128, 64)]:
         assert lib.mqa_is_supported(h, d, bs) == 0
 
 
@@ -90,8 +90,10 @@ def test_prefill_validation(lib):
     assert _prefill(lib, nulls, H=64) == mqa._native.MQA_ERR_INVALID_ARG  # supported; NULLs
     bad = _native.Tunables(block_m=8)  # 64 heads: at most 4 rows per wave
     assert _prefill(lib, nulls, H=64, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
-    assert _prefill(lib, nulls, D=64) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _prefill(lib, nulls, D=96) == mqa._native.MQA_ERR_UNSUPPORTED
     assert "num_heads" in mqa.last_error()
+    for h in (32, 64, 128):
+        assert _prefill(lib, nulls, H=h, D=64) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
     # empty problem: successful no-op, nothing dereferenced
     assert _prefill(lib, nulls, M=0) == 0
     assert _prefill(lib, nulls, N=0) == 0
@@ -119,6 +121,7 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls, bs=16) == mqa._native.MQA_ERR_INVALID_ARG  # supported; NULLs
     assert _decode(lib, nulls, bs=0) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, H=48) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, D=64) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, H=64, bs=16) == mqa._native.MQA_ERR_UNSUPPORTED
     bad = _native.Tunables(rows_per_block=2)  # 128 heads: one row per wave
     assert _decode(lib, nulls, H=128, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG

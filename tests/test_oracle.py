@@ -144,6 +144,8 @@ def _check_exact(out, vals, mags, ulps=64):
     (1, 1, 5, 7, "causal"),
     (2, 3, 6, 8, "misaligned"),
     (32, 128, 4, 6, "causal"),
+    (32, 64, 4, 6, "causal"),
+    (64, 64, 3, 5, "multi_req"),
     (3, 16, 8, 8, "empty"),
     (2, 8, 6, 9, "past_end"),
     (4, 8, 8, 12, "multi_req"),
