@@ -43,7 +43,7 @@ constexpr int kMaxBins = 4096;              // 12-bit digits
 constexpr int kSortCap = 8192;              // entries gathered into LDS and sorted
 constexpr int kCand = kSortCap - kMaxTopK;  // largest bucket gathered (keys above it < k)
 constexpr int kSample = 4096;               // entries sampled for the threshold
-constexpr int kBucketMax = 32;              // largest bucket sorted in registers
+constexpr int kBucketMax = 32;              // largest bucket whose entries rank themselves
 constexpr uint32_t kPosInfKey = 0xff800000u;  // order key of +inf
 constexpr int kCrowdMax = 2 * kThreads;     // largest bucket ranked by the whole block
 constexpr int kMaxCrowd = kSortCap / (kBucketMax + 1) + 1;  // crowded buckets at most
@@ -113,8 +113,10 @@ __device__ void find_threshold(TopkShared &sh, int nbins, int above, int k, int 
     const int w = nbins / 64;
     const int hi = nbins - lane * w;  // exclusive upper digit of this lane's span
     int mine = 0;
-    for (int d = hi - w; d < hi; ++d)
-        mine += (int)sh.hist[d];
+    // lane l starts its span at offset l: at each step the 64 lanes read 64
+    // different banks (in span order they would all hit one bank)
+    for (int j = 0; j < w; ++j)
+        mine += (int)sh.hist[hi - w + ((j + lane) & (w - 1))];
     const int incl = wave_inclusive_scan(mine, lane);
     const int excl = incl - mine;
     if (lane == 63)
@@ -257,48 +259,19 @@ __device__ void sort_desc(TopkShared &sh, int n2, int tid, int lane)
     __syncthreads();
 }
 
-// Sorting networks for small buckets: descending bitonic sort of N registers.
-template <int N>
-__device__ __forceinline__ void sort_small(uint64_t (&r)[N])
-{
-#pragma unroll
-    for (int size = 2; size <= N; size <<= 1)
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1)
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                if (i & stride)
-                    continue;
-                cmpx(r[i], r[i + stride], (i & size) == 0);
-            }
-}
-
-// Sort sh.sorted[start, start + m) descending, m <= N.
-template <int N>
-__device__ __forceinline__ void sort_bucket(TopkShared &sh, int start, int m)
-{
-    uint64_t r[N];
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-        r[j] = j < m ? sh.sorted[start + j] : 0ull;
-    sort_small<N>(r);
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-        if (j < m)
-            sh.sorted[start + j] = r[j];
-}
-
-
-// Bucket sort of sh.buf[0, n) into sh.sorted[0, n), descending.  Keys are
-// spread over kMaxBins buckets by (key - min key) >> shift, bucket 0 holding
-// the largest keys; a prefix sum places the buckets and every thread sorts
-// four buckets of up to kBucketMax entries in registers.  Larger buckets
-// (equal logits, such as the exact zeros of tokens whose head scores are all
-// negative) are ranked by the whole block, one bucket at a time: an entry's
-// place is the number of bucket entries above it (entries are distinct, as
-// their columns are).  Linear work for spread-out keys, where a bitonic sort
-// is n log^2 n.  Returns false, with nothing written, when some bucket holds
-// more than kCrowdMax entries; the caller then sorts sh.buf itself.
+// Bucket sort of sh.buf[0, n), descending, result in sh.buf (sh.sorted is
+// the scratch).  Keys are spread over kMaxBins buckets linearly in the
+// value, bucket 0 holding the largest; a prefix sum places the buckets and
+// the entries are scattered to them.  Then every entry of a bucket of up to
+// kBucketMax entries finds its place by itself: the number of entries of its
+// bucket above it (entries are distinct, as their columns are), so the work
+// is spread over entries rather than buckets and no lane waits on another's
+// large bucket.  Larger buckets (equal logits, such as the exact zeros of
+// tokens whose head scores are all negative) are ranked by the whole block,
+// one bucket at a time, the same way.  Linear work for spread-out keys, where
+// a bitonic sort is n log^2 n.  Returns false, with sh.buf unchanged, when
+// some bucket holds more than kCrowdMax entries; the caller then sorts
+// sh.buf itself.
 __device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int lane, int wave)
 {
     if (tid == 0) {
@@ -385,26 +358,24 @@ __device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int m = (int)c[j];
-        if (m <= 1)
-            continue;
-        if (m == 2) {
-            uint64_t a = sh.sorted[start[j]], b = sh.sorted[start[j] + 1];
-            cmpx(a, b, true);
-            sh.sorted[start[j]] = a;
-            sh.sorted[start[j] + 1] = b;
-        } else if (m <= 4) {
-            sort_bucket<4>(sh, start[j], m);
-        } else if (m <= 8) {
-            sort_bucket<8>(sh, start[j], m);
-        } else if (m <= 16) {
-            sort_bucket<16>(sh, start[j], m);
-        } else if (m <= kBucketMax) {
-            sort_bucket<kBucketMax>(sh, start[j], m);
-        } else {
+        if (m > kBucketMax) {
             const int slot = atomicAdd(&sh.ncrowd, 1);
             sh.crowd_start[slot] = start[j];
             sh.crowd_m[slot] = m;
         }
+    }
+    // sh.hist[b] now holds the end of bucket b (its cursor after the scatter)
+    for (int i = tid; i < n; i += kThreads) {
+        const uint64_t e = sh.sorted[i];
+        const int b = bucket_of(e);
+        const int end = (int)sh.hist[b];
+        const int st = b > 0 ? (int)sh.hist[b - 1] : 0;
+        if (end - st > kBucketMax)
+            continue;  // ranked below by the whole block
+        int r = 0;
+        for (int j = st; j < end; ++j)
+            r += sh.sorted[j] > e;
+        sh.buf[st + r] = e;
     }
     __syncthreads();
     const int ncrowd = sh.ncrowd;
@@ -430,14 +401,20 @@ __device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int 
             r0 += o > e0;
             r1 += o > e1;
         }
-        __syncthreads();
         if (tid < m)
-            sh.sorted[st + r0] = e0;
+            sh.buf[st + r0] = e0;
         if (tid + kThreads < m)
-            sh.sorted[st + r1] = e1;
-        __syncthreads();
+            sh.buf[st + r1] = e1;
     }
+    __syncthreads();
     return true;
+}
+
+// c ? a : b per component (a select of whole float4 objects can be lowered
+// through scratch memory).
+__device__ __forceinline__ float4 select4(bool c, float4 a, float4 b)
+{
+    return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
 // Call f(v, c) for the row in groups of four columns: v holds columns
@@ -459,8 +436,7 @@ __device__ __forceinline__ void for_each4(const float *x, int cols, int tid, F f
                 // unconditional in-bounds load (index clamped), then select,
                 // so the compiler keeps one 16-byte load per element
                 const int i = b + u * kThreads;
-                const float4 t = x4[min(i, n4 - 1)];
-                v[u] = i < n4 ? t : pad;
+                v[u] = select4(i < n4, x4[min(i, n4 - 1)], pad);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -521,8 +497,7 @@ __device__ __forceinline__ void load_batch(const float *x, int cols, int b, floa
         // unconditional in-bounds load (index clamped), then select, so the
         // compiler keeps one 16-byte load per element
         const int i = b + u * kThreads;
-        const float4 t = x4[min(i, n4 - 1)];
-        v[u] = i < n4 ? t : pad;
+        v[u] = select4(i < n4, x4[min(i, n4 - 1)], pad);
     }
 }
 
@@ -794,7 +769,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     }
     __syncthreads();
 
-    const uint64_t *order = sh.sorted;
     if (!bucket_sort(sh, n, tid, lane, wave)) {
         // Many equal or clustered keys: bitonic sort of the smallest power of
         // two >= n, padded with 0 (ranks last).
@@ -806,8 +780,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
             sh.buf[i] = 0ull;
         __syncthreads();
         sort_desc(sh, n2, tid, lane);
-        order = sh.buf;
     }
+    const uint64_t *order = sh.buf;
 
     const int nsel = min(n, k);
     for (int j = tid; j < k; j += kThreads)

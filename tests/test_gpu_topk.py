@@ -56,12 +56,52 @@ def test_row_families(cols, k):
     check(x, k, "families cols=%d k=%d" % (cols, k))
 
 
+@pytest.mark.parametrize("rows,cols", [(1, 32768), (3, 70001), (40, 131072)])
+def test_long_rows_with_runs_of_large_values(rows, cols):
+    """Long rows whose largest values sit in short runs spread over the row
+    (and in the row's last, odd columns)."""
+    rng = np.random.default_rng(540 + rows)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    n4 = cols // 4
+    for parts in range(2, 17):
+        for p in range(1, parts):
+            c = 4 * (n4 * p // parts)
+            x[:, max(c - 2, 0):c + 2] = 5.0 + rng.random((rows, min(c + 2, cols) - max(c - 2, 0)))
+    x[:, -3:] = 7.0
+    say("topk long rows=%d cols=%d" % (rows, cols))
+    for k in (1, 100, 2048):
+        check(x, k, "long rows=%d cols=%d k=%d" % (rows, cols, k))
+
+
+def test_skewed_and_overflowing_rows():
+    """Sorted rows (every large value at one end), a constant row (every entry
+    survives the sampled threshold, so the exact radix select takes over) and
+    a mostly masked row."""
+    rng = np.random.default_rng(550)
+    base = np.sort(rng.standard_normal(131072).astype(np.float32))
+    x = np.stack([base, base[::-1].copy(), np.full(131072, 0.25, np.float32),
+                  np.where(rng.random(131072) < 0.9, np.float32(-np.inf), base)])
+    say("topk skewed rows")
+    for k in (7, 2048):
+        check(x, k, "skewed k=%d" % k)
+
+
 def test_decode_logits_feed_topk():
     d = inputs.make_decode(3, 4, [5000, 700, 2100], 6000, seed=520, poison=True)
     say("topk of decode logits")
     logits = np.ascontiguousarray(run_decode(d))
     for k in (1, 64, 512, 2048):
         check(logits, k, "decode logits k=%d" % k)
+
+
+def test_long_decode_logits():
+    """Decode logits of long sequences (rows of 65536 columns, ragged windows,
+    so rows end in runs of -inf)."""
+    d = inputs.make_decode(2, 3, [65536, 40000], 65536, seed=521)
+    logits = np.ascontiguousarray(run_decode(d))
+    say("topk of long decode logits")
+    for k in (512, 2048):
+        check(logits, k, "long decode logits k=%d" % k)
 
 
 def test_many_rows_and_odd_widths():
