@@ -44,7 +44,7 @@ def _decode_window(d):
     return p <= bound[:, None]
 
 
-@pytest.mark.parametrize("idx", [0, 3])
+@pytest.mark.parametrize("idx", [0, 3, 13, 15])
 def test_prefill_workload(idx):
     t0 = time.time()
     p = inputs.make_config(idx)
@@ -61,7 +61,7 @@ def test_prefill_workload(idx):
     assert_parity(out[rows], ref, mag, f"workload{idx}")
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4])
+@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14])
 def test_decode_workload(idx):
     t0 = time.time()
     d = inputs.make_config(idx, poison=True)
