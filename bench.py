@@ -84,6 +84,9 @@ TOPK_WORKLOADS = {5: (2, 2048), 6: (2, 512)}
 # K-cache insert workloads: index -> (tokens, bf16 input).  4096 tokens is the
 # long prefill chunk's K; 96 is one decode step of the MTP workload (16 x 6).
 KCACHE_WORKLOADS = {7: (4096, False), 8: (96, True)}
+# Fused decode top-k workloads: index -> (decode workload, k); the indices
+# only, the logits never written.
+FUSED_WORKLOADS = {16: (2, 2048), 17: (2, 512)}
 
 
 class Workload:
@@ -205,9 +208,49 @@ class KcacheWorkload:
         kcache_quantize_insert(s["k"], s["slots"], s["cache"])
 
 
+class FusedTopkWorkload:
+    """Paged decode fused with the top-k of its logits (paged_mqa_topk_decode).
+    Essential bytes: the decode's inputs (K and scales once, Q, weights, used
+    table entries, context lengths) plus the indices written."""
+
+    def __init__(self, idx, hot, tunables=None):
+        import torch
+        from sparse_attention_indexer_scaled_amd import paged_mqa_topk_workspace_size
+        decode_idx, k = FUSED_WORKLOADS[idx]
+        src = Workload(decode_idx, hot, tunables)
+        h = src.host
+        rows = h.B * h.next_n
+        self.idx = idx
+        self.kind = "fused_topk"
+        self.k = k
+        self.cfg = {"kind": "fused_topk", "name": "decode_topk_k%d_%s" % (k, src.cfg["name"][7:]),
+                    "k": k}
+        self.host = h
+        self.sets = src.sets
+        self.nsets = src.nsets
+        self.bytes = src.bytes - rows * h.max_model_len * 4 + rows * k * 4
+        self.pairs = src.pairs
+        self.flops = src.flops
+        self.tun = tunables
+        self.outs = [torch.empty((rows, k), dtype=torch.int32, device="cuda")
+                     for _ in range(self.nsets)]
+        self.ws = torch.empty(paged_mqa_topk_workspace_size(h.B, h.next_n, h.max_model_len),
+                              dtype=torch.uint8, device="cuda")
+
+    def call(self, i):
+        from sparse_attention_indexer_scaled_amd import paged_mqa_topk_decode
+        s = self.sets[i % self.nsets]
+        paged_mqa_topk_decode(s["q"], s["cache"], s["w"], s["ctx"], s["bt"],
+                              self.host.max_model_len, self.k, kv_block_size=self.host.block_size,
+                              indices=self.outs[i % self.nsets], workspace=self.ws,
+                              tunables=self.tun, preshuffle=self.host.preshuffle)
+
+
 def make_workload(idx, hot, tunables=None):
     if idx in TOPK_WORKLOADS:
         return TopkWorkload(idx, hot)
+    if idx in FUSED_WORKLOADS:
+        return FusedTopkWorkload(idx, hot, tunables)
     if idx in KCACHE_WORKLOADS:
         return KcacheWorkload(idx, hot)
     return Workload(idx, hot, tunables)
@@ -541,7 +584,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15) if i != args.workload]
+        [i for i in (1, 4, 3, 0, 5, 6, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15) if i != args.workload]
     results, head = {}, None
     for idx in order:
         wl = make_workload(idx, args.hot, tun)
@@ -561,16 +604,18 @@ def main():
     r = results[wl.cfg["name"]]
     h = wl.host
     decode = wl.kind == "decode"
-    hbm_bound = wl.kind in ("decode", "topk", "kcache")
+    hbm_bound = wl.kind in ("decode", "topk", "kcache", "fused_topk")
     if wl.kind == "kcache":
         config = {"workload": wl.cfg["name"], "tokens": wl.cfg["tokens"], "cold": not args.hot}
     elif wl.kind == "topk":
         config = {"workload": wl.cfg["name"], "rows": wl.cfg["rows"], "cols": wl.cfg["cols"],
                   "k": wl.k, "cold": not args.hot}
-    elif decode:
+    elif decode or wl.kind == "fused_topk":
         config = {"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
                   "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
                   "heads": h.H, "head_dim": 128, "kv_block_size": h.block_size, "cold": not args.hot}
+        if wl.kind == "fused_topk":
+            config["k"] = wl.k
     else:
         config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": h.H, "head_dim": 128,
                   "cold": not args.hot}

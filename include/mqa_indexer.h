@@ -32,6 +32,7 @@
 #ifndef MQA_INDEXER_H
 #define MQA_INDEXER_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -197,6 +198,47 @@ int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const
  */
 int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *indices,
                      hipStream_t stream);
+
+/*
+ * Fused paged decode + row-wise top-k: the indices mqa_topk_indices would
+ * return for the logits paged_mqa_logits_decode (clean_logits = 1) would
+ * write, without writing those logits (the top-k is the indexer's consumer:
+ * aiter PR 5047 page, "Integration"; writing the logits only to read them back
+ * is the traffic this avoids).  Same arguments and preconditions as
+ * paged_mqa_logits_decode, with
+ *
+ *   indices    [batch * next_n, k]  int32, written (same order, ties and -1
+ *              padding as mqa_topk_indices); 1 <= k <= 2048
+ *   workspace  DEVICE memory of at least
+ *              paged_mqa_topk_workspace_size(batch, next_n, max_model_len)
+ *              bytes (about 8 bytes per row and position: 101 MB for 96 rows
+ *              of 131072), 256-byte aligned, owned by the caller; contents on
+ *              entry do not matter and are clobbered.  Calls that overlap on one
+ *              workspace race.
+ *
+ * Four kernels on `stream`: a decode of 16 evenly spaced runs of 256
+ * positions per sequence (the sample), per-row thresholds from it, the decode
+ * of every position keeping only the entries at or above the row's threshold,
+ * and a per-row select and sort.  A row whose kept entries cannot hold its top
+ * k (the sample misjudged it) is recomputed in full by its select workgroup
+ * (its logits into its workspace segment, then an exact radix select), so the
+ * output is exact for every input; such rows only take longer.
+ * Supported: num_heads 32, head_dim 128, kv_block_size 64 (either kv_layout),
+ * ring_depth tunable 0 or 3, a KV split of at most 1024.  Errors as for
+ * paged_mqa_logits_decode, plus: k out of range, NULL or misaligned indices or
+ * workspace, a workspace smaller than asked for -> MQA_ERR_INVALID_ARG; other
+ * head counts or block sizes -> MQA_ERR_UNSUPPORTED.
+ */
+int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *weights,
+                          const int32_t *context_lens, const int32_t *block_tables,
+                          int32_t *indices, int batch, int next_n, int num_heads, int head_dim,
+                          int kv_block_size, int kv_layout, int num_blocks,
+                          int max_blocks_per_seq, int max_model_len, int k, void *workspace,
+                          size_t workspace_bytes, const mqa_tunables *tun, hipStream_t stream);
+
+/* Workspace bytes paged_mqa_topk_decode needs (0 for sizes it rejects or
+ * treats as a no-op).  Host-only, never fails. */
+size_t paged_mqa_topk_workspace_size(int batch, int next_n, int max_model_len);
 
 #define MQA_DTYPE_FP32 0
 #define MQA_DTYPE_BF16 1

@@ -21,5 +21,7 @@ from ._native import (  # noqa: F401
     load_library,
     mqa_logits_prefill,
     paged_mqa_logits_decode,
+    paged_mqa_topk_decode,
+    paged_mqa_topk_workspace_size,
     topk_indices,
 )

@@ -24,7 +24,8 @@ MQA_ERR_LAUNCH = -3
 MQA_ERR_DEVICE = -4
 
 EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode",
-            "mqa_topk_indices", "mqa_kcache_quantize_insert", "mqa_last_error")
+            "mqa_topk_indices", "paged_mqa_topk_decode", "paged_mqa_topk_workspace_size",
+            "mqa_kcache_quantize_insert", "mqa_last_error")
 MQA_DTYPE_FP32 = 0
 MQA_DTYPE_BF16 = 1
 MQA_KV_SLOT_MAJOR = 0
@@ -68,6 +69,11 @@ def load_library(path: str = LIB_PATH):
     lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, P]
     lib.mqa_topk_indices.restype = I
     lib.mqa_topk_indices.argtypes = [P, I, I, I, P, P]
+    lib.paged_mqa_topk_decode.restype = I
+    lib.paged_mqa_topk_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P,
+                                          ctypes.c_size_t, P, P]
+    lib.paged_mqa_topk_workspace_size.restype = ctypes.c_size_t
+    lib.paged_mqa_topk_workspace_size.argtypes = [I, I, I]
     lib.mqa_kcache_quantize_insert.restype = I
     lib.mqa_kcache_quantize_insert.argtypes = [P, I, P, P, I, I, I, I, I, P]
     _lib = lib
@@ -196,6 +202,51 @@ def topk_indices(logits: torch.Tensor, k: int, indices: Optional[torch.Tensor] =
     rc = load_library().mqa_topk_indices(
         _dev(logits, "logits", torch.float32), rows, cols, int(k),
         _dev(indices, "indices", torch.int32), _stream(stream, logits.device))
+    _check(rc)
+    return indices
+
+
+def paged_mqa_topk_workspace_size(batch: int, next_n: int, max_model_len: int) -> int:
+    return int(load_library().paged_mqa_topk_workspace_size(int(batch), int(next_n),
+                                                              int(max_model_len)))
+
+
+def paged_mqa_topk_decode(q_fp8: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
+                          context_lens: torch.Tensor, block_tables: torch.Tensor,
+                          max_model_len: int, k: int, kv_block_size: int = 64,
+                          indices: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          tunables: Optional[Tunables] = None, stream=None,
+                          preshuffle: bool = False) -> torch.Tensor:
+    """The top-k indices [B*next_n, k] int32 of the decode logits (as
+    topk_indices(paged_mqa_logits_decode(...), k)), without writing the logits.
+    workspace: a uint8 device tensor of at least paged_mqa_topk_workspace_size
+    bytes (allocated from torch's caching allocator when not given)."""
+    q = _bytes(q_fp8, "q_fp8")
+    cache = _bytes(kv_cache, "kv_cache")
+    B, next_n, H, D = q.shape
+    if cache.dim() != 2 or cache.shape[1] != kv_block_size * (D + 4):
+        raise ValueError("kv_cache must be [num_blocks, kv_block_size*(head_dim+4)] bytes")
+    if weights.shape != (B * next_n, H) or context_lens.shape != (B,):
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks_per_seq]")
+    rows = B * next_n
+    if indices is None:
+        indices = torch.empty((rows, k), dtype=torch.int32, device=q.device)
+    if indices.shape != (rows, k):
+        raise ValueError("indices must be [B*next_n, k]")
+    if workspace is None:
+        need = paged_mqa_topk_workspace_size(B, next_n, max_model_len)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws = _bytes(workspace, "workspace")
+    rc = load_library().paged_mqa_topk_decode(
+        _dev(q, "q_fp8"), _dev(cache, "kv_cache"), _dev(weights, "weights", torch.float32),
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), _dev(indices, "indices", torch.int32),
+        B, next_n, H, D, int(kv_block_size), _layout(preshuffle), cache.shape[0],
+        block_tables.shape[1], int(max_model_len), int(k), _dev(ws, "workspace"), ws.numel(),
+        _tun(tunables), _stream(stream, q.device))
     _check(rc)
     return indices
 

@@ -199,13 +199,20 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     return ok();
 }
 
-extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache,
-                                       const float *weights, const int32_t *context_lens,
-                                       const int32_t *block_tables, float *logits, int batch,
-                                       int next_n, int num_heads, int head_dim, int kv_block_size,
-                                       int kv_layout, int num_blocks, int max_blocks_per_seq,
-                                       int max_model_len, int clean_logits,
-                                       const mqa_tunables *tun, hipStream_t stream)
+namespace {
+
+constexpr int kNoop = 1;  // prepare_decode: valid arguments, nothing to do
+
+// Validate the paged-decode arguments shared by the logits call and the
+// fused top-k, and fill the launch (pointers and the launch heuristic).
+// Returns MQA_OK, kNoop, or a (recorded) error code.  `logits` is only
+// checked when need_logits.
+int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *weights,
+                   const int32_t *context_lens, const int32_t *block_tables, float *logits,
+                   bool need_logits, int batch, int next_n, int num_heads, int head_dim,
+                   int kv_block_size, int kv_layout, int num_blocks, int max_blocks_per_seq,
+                   int max_model_len, int clean_logits, const mqa_tunables *tun,
+                   mqa::DecodeLaunch &p)
 {
     if (batch < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_model_len < 0)
         return fail(MQA_ERR_INVALID_ARG, "negative size argument");
@@ -236,16 +243,18 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
                     "(0 or 4 unless 32 heads and kv_block_size 64), num_warps 0",
                     max_rows);
     if (batch == 0 || max_model_len == 0)
-        return ok();
-    if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables || !logits)
+        return kNoop;
+    if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables ||
+        (need_logits && !logits))
         return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
     if (!aligned(q_fp8, 16) || !aligned(kv_cache, 16) || !aligned(weights, 16) ||
-        !aligned(logits, 16) || !aligned(context_lens, 4) || !aligned(block_tables, 4))
+        (need_logits && !aligned(logits, 16)) || !aligned(context_lens, 4) ||
+        !aligned(block_tables, 4))
         return fail(MQA_ERR_INVALID_ARG, "data pointers must be 16-byte aligned, int32 arrays 4-byte");
     if (int rc = check_device())
         return rc;
 
-    mqa::DecodeLaunch p;
+    p = mqa::DecodeLaunch{};
     p.q = q_fp8;
     p.cache = kv_cache;
     p.weights = weights;
@@ -292,9 +301,108 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
     if (trace_on())
         std::fprintf(stderr, "[mqa] decode B=%d next_n=%d mml=%d rows=%d split_kv=%d depth=%d\n", batch,
                      next_n, max_model_len, p.rows, p.split_kv, p.depth);
+    return MQA_OK;
+}
+
+} // namespace
+
+extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_cache,
+                                       const float *weights, const int32_t *context_lens,
+                                       const int32_t *block_tables, float *logits, int batch,
+                                       int next_n, int num_heads, int head_dim, int kv_block_size,
+                                       int kv_layout, int num_blocks, int max_blocks_per_seq,
+                                       int max_model_len, int clean_logits,
+                                       const mqa_tunables *tun, hipStream_t stream)
+{
+    mqa::DecodeLaunch p;
+    const int rc = prepare_decode(q_fp8, kv_cache, weights, context_lens, block_tables, logits, true,
+                                  batch, next_n, num_heads, head_dim, kv_block_size, kv_layout,
+                                  num_blocks, max_blocks_per_seq, max_model_len, clean_logits, tun, p);
+    if (rc == kNoop)
+        return ok();
+    if (rc != MQA_OK)
+        return rc;
     hipError_t e = mqa::launch_decode(p, stream);
     if (e != hipSuccess)
         return fail(MQA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" size_t paged_mqa_topk_workspace_size(int batch, int next_n, int max_model_len)
+{
+    if (batch <= 0 || next_n < 1 || next_n > 8 || max_model_len <= 0)
+        return 0;
+    return mqa::fused_workspace(nullptr, batch * next_n, max_model_len).bytes;
+}
+
+extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cache,
+                                     const float *weights, const int32_t *context_lens,
+                                     const int32_t *block_tables, int32_t *indices, int batch,
+                                     int next_n, int num_heads, int head_dim, int kv_block_size,
+                                     int kv_layout, int num_blocks, int max_blocks_per_seq,
+                                     int max_model_len, int k, void *workspace,
+                                     size_t workspace_bytes, const mqa_tunables *tun,
+                                     hipStream_t stream)
+{
+    if (k < 1 || k > mqa::kMaxTopK)
+        return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
+    if (tun && tun->ring_depth != 0 && tun->ring_depth != 3)
+        return fail(MQA_ERR_INVALID_ARG, "the fused top-k runs the default ring depth (0 or 3)");
+    if (num_heads != 32 || head_dim != 128 || kv_block_size != 64)
+        return fail(MQA_ERR_UNSUPPORTED, "the fused top-k supports num_heads 32, head_dim 128 and "
+                    "kv_block_size 64 (got %d, %d, %d)", num_heads, head_dim, kv_block_size);
+    if (batch > 0 && max_model_len > 0 && next_n >= 1 && next_n <= 8) {
+        if (!indices || !workspace)
+            return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
+        if (!aligned(indices, 4) || !aligned(workspace, 256))
+            return fail(MQA_ERR_INVALID_ARG, "indices must be 4-byte aligned, workspace 256-byte");
+        const size_t need = paged_mqa_topk_workspace_size(batch, next_n, max_model_len);
+        if (workspace_bytes < need)
+            return fail(MQA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes "
+                        "paged_mqa_topk_workspace_size asks for", workspace_bytes, need);
+    }
+    mqa::DecodeLaunch p;
+    const int rc = prepare_decode(q_fp8, kv_cache, weights, context_lens, block_tables, nullptr,
+                                  false, batch, next_n, num_heads, head_dim, kv_block_size,
+                                  kv_layout, num_blocks, max_blocks_per_seq, max_model_len, 1, tun,
+                                  p);
+    if (rc == kNoop)
+        return ok();
+    if (rc != MQA_OK)
+        return rc;
+    if (p.split_kv > mqa::kFusedMaxSplit)
+        return fail(MQA_ERR_INVALID_ARG, "the fused top-k takes split_kv <= %d (got %d)",
+                    mqa::kFusedMaxSplit, p.split_kv);
+    const int rows = batch * next_n;
+    const mqa::FusedWorkspace w = mqa::fused_workspace(workspace, rows, max_model_len);
+    mqa::FusedTopkLaunch f{&w,      context_lens, indices, batch,   next_n,
+                           max_model_len, k,   p.split_kv, q_fp8, kv_cache,
+                           weights, block_tables, max_blocks_per_seq, p.tiled};
+    hipError_t e;
+    // 1. the sample: kFusedSampleChunks runs of steps per sequence
+    mqa::DecodeLaunch ps = p;
+    ps.mode = 1;
+    ps.split_kv = mqa::kFusedSampleChunks;
+    ps.sample = w.sample;
+    e = mqa::launch_decode(ps, stream);
+    // 2. per-row thresholds
+    if (e == hipSuccess)
+        e = mqa::launch_fused_threshold(f, stream);
+    // 3. the filtering decode
+    if (e == hipSuccess) {
+        mqa::DecodeLaunch pf = p;
+        pf.mode = 2;
+        pf.threshold = w.threshold;
+        pf.entries = w.entries;
+        pf.counts = w.counts;
+        pf.ent_stride = w.ent_stride;
+        e = mqa::launch_decode(pf, stream);
+    }
+    // 4. select and sort; a row the sample misjudged is recomputed in full
+    if (e == hipSuccess)
+        e = mqa::launch_fused_select(f, stream);
+    if (e != hipSuccess)
+        return fail(MQA_ERR_LAUNCH, "fused top-k launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -33,11 +33,23 @@
 // cannot reach an output.
 #include "device.h"
 #include "launch.h"
+#include "order_key.h"
 
 namespace mqa {
 namespace {
 
 constexpr int kSlotBytes = kBlockBytes;  // ring slot: one 64-token step, K rows + scales
+constexpr int kSampleChunks = kFusedSampleChunks;
+constexpr int kSampleSteps = kFusedSampleSteps;
+constexpr int kSampleCols = kFusedSampleCols;
+
+// LDS bytes of a workgroup's ring (and, for per-token blocks, its table
+// ring).
+template <int D, int BS>
+constexpr int ring_lds_bytes()
+{
+    return D * kSlotBytes + (BS == 1 ? (2 * D - 2) * kStep * 4 : 0);
+}
 constexpr int kChunks = kDim * kBlock / 1024 + 1;  // 8 x 1 KiB of K + 1 x 256 B of scales
 
 // Sizes and launch shape; the pointers are separate __restrict__ kernel
@@ -50,7 +62,23 @@ struct DecodeArgs {
     int groups;
     int split;
     int tiled;  // K rows of a block in the preshuffled (16,16) order
+    // Fused top-k (see the kernel's modes; unused by the plain logits call):
+    float *sample;                // sample mode: [rows][kSampleCols]
+    const uint32_t *threshold;    // filter mode: [rows] order-key thresholds
+    uint64_t *entries;            // filter mode: [rows][ent_stride]
+    int *counts;                  // filter mode: [rows][split]
+    int64_t ent_stride;
 };
+
+// Kernel modes.  kLogits: the op's output.  The fused top-k adds two:
+// kSample computes kSampleChunks evenly spaced runs of kSampleSteps steps of
+// each sequence (the sample its thresholds are drawn from) into a small
+// buffer, -inf outside the windows; kFilter computes every step like kLogits
+// but, instead of storing the logits, appends the (key, column) entries of
+// each row at or above the row's threshold to the workgroup's own segment of
+// the row (it starts at the workgroup's first column, so it can never
+// overflow), and stores their count.
+enum DecodeMode { kLogits = 0, kSample = 1, kFilter = 2 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -288,7 +316,7 @@ __device__ __forceinline__ void read_wait(KStep &k)
                  : "memory");
 }
 
-template <int R, int G, int D, int BS, int HT>
+template <int R, int G, int D, int BS, int HT, int MODE = kLogits>
 __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restrict__ qbuf,
                                                         const uint8_t *__restrict__ cache,
                                                         const float *__restrict__ wbuf,
@@ -313,8 +341,16 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
     // row's bound is ctx - 1), so all of them execute the same barriers.
     const int nvalid = max(min(ctx, mml), 0);
     const int nsteps = (nvalid + kStep - 1) / kStep;
-    const int st0 = (int)((int64_t)nsteps * s / a.split);
-    const int st1 = (int)((int64_t)nsteps * (s + 1) / a.split);
+    int st0, st1;
+    if constexpr (MODE == kSample) {
+        // chunk s of kSampleChunks (a.split): kSampleSteps steps, evenly spaced
+        const int span = max(nsteps - kSampleSteps, 0);
+        st0 = (int)((int64_t)span * s / (kSampleChunks - 1));
+        st1 = min(st0 + kSampleSteps, nsteps);
+    } else {
+        st0 = (int)((int64_t)nsteps * s / a.split);
+        st1 = (int)((int64_t)nsteps * (s + 1) / a.split);
+    }
     const int64_t row_base = (int64_t)b * a.next_n + row0;
     float *out = logits + row_base * mml;
     const int t = lane & 31;
@@ -325,6 +361,19 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         constexpr int H = kHeads * HT;
         Frag q[R][HT];
         Weights16 w[R][HT];
+        // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f)
+        // and the entries kept so far for it (each row belongs to one wave, and
+        // within it to one half of the lanes, so the count needs no atomics)
+        float fthr[NP];
+        int kept[NP];
+        if constexpr (MODE == kFilter) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const uint32_t tk = a.threshold[row_base + min(2 * i + half, nrows - 1)];
+                fthr[i] = tk == 0u ? __builtin_inff() : key_float(tk);
+                kept[i] = 0;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             // a short last group computes its missing rows as copies of its
@@ -351,6 +400,42 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         const bool clean = a.clean != 0;
         auto store_step = [&](int step, const float (&tot)[2][NP]) {
             const int p0 = step * kStep;
+            if constexpr (MODE == kSample) {
+                // columns of chunk s: [s kSampleSteps 64, (s + 1) kSampleSteps 64)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int p = p0 + h * kTile + t;
+                    const int c = s * kSampleSteps * kStep + (p - st0 * kStep);
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        const bool valid = p <= obound[i] && p < mml;
+                        if (ostore[i])
+                            a.sample[(row_base + 2 * i + half) * kSampleCols + c] =
+                                valid ? tot[h][i] : ninf;
+                    }
+                }
+                return;
+            }
+            if constexpr (MODE == kFilter) {
+                const uint32_t lt = (1u << t) - 1u;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int p = p0 + h * kTile + t;
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        const bool keep =
+                            ostore[i] && p <= obound[i] && p < mml && tot[h][i] >= fthr[i];
+                        const uint64_t bal = __ballot(keep);
+                        // lanes 0..31 hold row 2i, lanes 32..63 row 2i + 1
+                        const uint32_t mine = half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+                        if (keep)
+                            a.entries[(row_base + 2 * i + half) * a.ent_stride + st0 * kStep +
+                                      kept[i] + __popc(mine & lt)] = fused_entry(tot[h][i], p);
+                        kept[i] += __popc(mine);
+                    }
+                }
+                return;
+            }
             if (p0 + kStep - 1 <= first_bound && p0 + kStep <= mml) {
                 // every column of the step is inside every row's window
 #pragma unroll
@@ -464,9 +549,30 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
             step_scores<R, HT>(kb, q, w, prev_tot);
         }
         store_step(st1 - 1, prev_tot);
+        if constexpr (MODE == kFilter) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                if (ostore[i] && t == 0)
+                    a.counts[(row_base + 2 * i + half) * a.split + s] = kept[i];
+        }
         // No global->LDS load may still be in flight once the workgroup ends
         // and its LDS goes to the next workgroup.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if constexpr (MODE == kSample) {
+        // the chunk's columns past its last step (short sequences) are -inf
+        const int done = max(st1 - st0, 0) * kStep;
+        for (int r = 0; r < nrows; ++r)
+            for (int c = done + lane; c < kSampleSteps * kStep; c += 64)
+                a.sample[(row_base + r) * kSampleCols + s * kSampleSteps * kStep + c] = ninf;
+        return;
+    }
+    if constexpr (MODE == kFilter) {
+        // a workgroup with no step (empty sequence) keeps nothing
+        if (st0 >= st1 && lane == 0)
+            for (int r = 0; r < nrows; ++r)
+                a.counts[(row_base + r) * a.split + s] = 0;
+        return;
     }
     if (a.clean) {
         const int64_t f0 = min((int64_t)nsteps * kStep, (int64_t)mml);
@@ -475,18 +581,24 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
     }
 }
 
-template <int R, int G, int D, int BS, int HT = 1>
+template <int R, int G, int D, int BS, int HT = 1, int MODE = kLogits>
 hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
-    const size_t lds = (size_t)D * kSlotBytes + (BS == 1 ? (size_t)(2 * D - 2) * kStep * 4 : 0);
-    hipLaunchKernelGGL((decode_kernel<R, G, D, BS, HT>), dim3(grid), dim3(64 * G), lds, stream, p.q,
-                       p.cache, p.weights, p.context_lens, p.block_tables, p.logits, a);
+    const size_t lds = (size_t)ring_lds_bytes<D, BS>();
+    hipLaunchKernelGGL((decode_kernel<R, G, D, BS, HT, MODE>), dim3(grid), dim3(64 * G), lds, stream,
+                       p.q, p.cache, p.weights, p.context_lens, p.block_tables, p.logits, a);
     return hipGetLastError();
 }
 
-template <int R, int G>
+template <int R, int G, int MODE>
 hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
+    if constexpr (MODE != kLogits) {
+        // the fused top-k's modes: 32 heads, 64-token blocks, the default ring
+        if (p.block_size != 64 || p.depth != 3)
+            return hipErrorInvalidValue;
+        return launch_rgdb<R, G, 3, 64, 1, MODE>(p, a, grid, stream);
+    }
     if (p.block_size == 64) {
         switch (p.depth) {
         case 2: return launch_rgdb<R, G, 2, 64>(p, a, grid, stream);
@@ -509,6 +621,32 @@ hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipSt
     }
 }
 
+// (rows, row groups) pairs that next_n in 1..8 can produce
+template <int MODE>
+hipError_t launch_mode(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
+{
+    switch (p.rows * 16 + a.groups) {
+    case 1 * 16 + 1: return launch_rg<1, 1, MODE>(p, a, grid, stream);
+    case 1 * 16 + 2: return launch_rg<1, 2, MODE>(p, a, grid, stream);
+    case 1 * 16 + 3: return launch_rg<1, 3, MODE>(p, a, grid, stream);
+    case 1 * 16 + 4: return launch_rg<1, 4, MODE>(p, a, grid, stream);
+    case 1 * 16 + 5: return launch_rg<1, 5, MODE>(p, a, grid, stream);
+    case 1 * 16 + 6: return launch_rg<1, 6, MODE>(p, a, grid, stream);
+    case 1 * 16 + 7: return launch_rg<1, 7, MODE>(p, a, grid, stream);
+    case 1 * 16 + 8: return launch_rg<1, 8, MODE>(p, a, grid, stream);
+    case 2 * 16 + 1: return launch_rg<2, 1, MODE>(p, a, grid, stream);
+    case 2 * 16 + 2: return launch_rg<2, 2, MODE>(p, a, grid, stream);
+    case 2 * 16 + 3: return launch_rg<2, 3, MODE>(p, a, grid, stream);
+    case 2 * 16 + 4: return launch_rg<2, 4, MODE>(p, a, grid, stream);
+    case 3 * 16 + 1: return launch_rg<3, 1, MODE>(p, a, grid, stream);
+    case 3 * 16 + 2: return launch_rg<3, 2, MODE>(p, a, grid, stream);
+    case 3 * 16 + 3: return launch_rg<3, 3, MODE>(p, a, grid, stream);
+    case 4 * 16 + 1: return launch_rg<4, 1, MODE>(p, a, grid, stream);
+    case 4 * 16 + 2: return launch_rg<4, 2, MODE>(p, a, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 } // namespace
 
 int decode_ring_bytes(int depth) { return depth * kSlotBytes; }
@@ -523,7 +661,14 @@ hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream)
     a.groups = (p.next_n + p.rows - 1) / p.rows;
     a.split = p.split_kv;
     a.tiled = p.tiled;
+    a.sample = p.sample;
+    a.threshold = p.threshold;
+    a.entries = p.entries;
+    a.counts = p.counts;
+    a.ent_stride = p.ent_stride;
     const int grid = p.batch * a.split;
+    if (p.mode != kLogits && p.head_tiles != 1)
+        return hipErrorInvalidValue;
     if (p.head_tiles == 2) {
         // 64 heads: at most 2 rows per wave (Q and weights take 64 VGPRs a row)
         switch (p.rows * 16 + a.groups) {
@@ -556,25 +701,10 @@ hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream)
         default: return hipErrorInvalidValue;
         }
     }
-    // (rows, row groups) pairs that next_n in 1..8 can produce
-    switch (p.rows * 16 + a.groups) {
-    case 1 * 16 + 1: return launch_rg<1, 1>(p, a, grid, stream);
-    case 1 * 16 + 2: return launch_rg<1, 2>(p, a, grid, stream);
-    case 1 * 16 + 3: return launch_rg<1, 3>(p, a, grid, stream);
-    case 1 * 16 + 4: return launch_rg<1, 4>(p, a, grid, stream);
-    case 1 * 16 + 5: return launch_rg<1, 5>(p, a, grid, stream);
-    case 1 * 16 + 6: return launch_rg<1, 6>(p, a, grid, stream);
-    case 1 * 16 + 7: return launch_rg<1, 7>(p, a, grid, stream);
-    case 1 * 16 + 8: return launch_rg<1, 8>(p, a, grid, stream);
-    case 2 * 16 + 1: return launch_rg<2, 1>(p, a, grid, stream);
-    case 2 * 16 + 2: return launch_rg<2, 2>(p, a, grid, stream);
-    case 2 * 16 + 3: return launch_rg<2, 3>(p, a, grid, stream);
-    case 2 * 16 + 4: return launch_rg<2, 4>(p, a, grid, stream);
-    case 3 * 16 + 1: return launch_rg<3, 1>(p, a, grid, stream);
-    case 3 * 16 + 2: return launch_rg<3, 2>(p, a, grid, stream);
-    case 3 * 16 + 3: return launch_rg<3, 3>(p, a, grid, stream);
-    case 4 * 16 + 1: return launch_rg<4, 1>(p, a, grid, stream);
-    case 4 * 16 + 2: return launch_rg<4, 2>(p, a, grid, stream);
+    switch (p.mode) {
+    case kLogits: return launch_mode<kLogits>(p, a, grid, stream);
+    case kSample: return launch_mode<kSample>(p, a, grid, stream);
+    case kFilter: return launch_mode<kFilter>(p, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -45,7 +45,54 @@ struct DecodeLaunch {
     int block_size;  // tokens per cache block: 1, 16, 64 or 128
     int head_tiles;  // num_heads / 32: 1, 2 or 4 (2 and 4: block size 64, depth 4)
     int tiled;       // 1: K rows in the preshuffled (16,16) order (block size >= 16)
+    // fused top-k only (zero / NULL for the logits call):
+    int mode;              // 0 logits, 1 sample, 2 filter (modes 1, 2: 32 heads, block 64, depth 3)
+    float *sample;         // [rows][kFusedSampleCols]
+    const uint32_t *threshold;  // [rows]
+    uint64_t *entries;     // [rows][ent_stride]
+    int *counts;           // [rows][split_kv]
+    int64_t ent_stride;
 };
+
+// Fused decode top-k: sample shape (chunks of steps per sequence), largest KV
+// split it accepts, and its workspace layout.
+constexpr int kFusedSampleChunks = 16;
+constexpr int kFusedSampleSteps = 4;
+constexpr int kFusedSampleCols = kFusedSampleChunks * kFusedSampleSteps * 64;
+constexpr int kFusedMaxSplit = 1024;
+
+struct FusedWorkspace {
+    uint64_t *entries;    // [rows][ent_stride]; a recomputed row's fp32 logits go to its own
+    int *counts;          // [rows][kFusedMaxSplit]
+    uint32_t *threshold;  // [rows]
+    int *recomputed;      // [rows]: 1 where the select recomputed the row in full
+    float *sample;        // [rows][kFusedSampleCols]
+    int64_t ent_stride;
+    size_t bytes;
+};
+
+inline size_t fused_align(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Layout of the fused top-k workspace at `base` (NULL: sizes only).
+inline FusedWorkspace fused_workspace(void *base, int rows, int64_t mml)
+{
+    FusedWorkspace w;
+    w.ent_stride = (mml + 63) / 64 * 64;
+    size_t off = 0;
+    char *b = static_cast<char *>(base);
+    auto take = [&](size_t n) {
+        char *q = b ? b + off : nullptr;
+        off = fused_align(off + n);
+        return q;
+    };
+    w.entries = reinterpret_cast<uint64_t *>(take((size_t)rows * w.ent_stride * 8));
+    w.counts = reinterpret_cast<int *>(take((size_t)rows * kFusedMaxSplit * 4));
+    w.threshold = reinterpret_cast<uint32_t *>(take((size_t)rows * 4));
+    w.recomputed = reinterpret_cast<int *>(take((size_t)rows * 4));
+    w.sample = reinterpret_cast<float *>(take((size_t)rows * kFusedSampleCols * 4));
+    w.bytes = off;
+    return w;
+}
 
 // Largest k of the row-wise top-k.
 constexpr int kMaxTopK = 2048;
@@ -56,6 +103,26 @@ struct TopkLaunch {
     int rows;
     int cols;
     int k;  // 1..kMaxTopK
+};
+
+// Fused top-k steps after the sampling decode and before the filtering one
+// (thresholds from the sample), and after it (select, or flag the row).
+struct FusedTopkLaunch {
+    const FusedWorkspace *ws;
+    const int32_t *context_lens;
+    int32_t *indices;
+    int batch;
+    int next_n;
+    int mml;
+    int k;
+    int split;  // the filtering decode's KV split
+    // what a row needs to be recomputed in full (64-token blocks, 32 heads)
+    const uint8_t *q;
+    const uint8_t *cache;
+    const float *weights;
+    const int32_t *block_tables;
+    int max_blocks_per_seq;
+    int tiled;
 };
 
 struct KcacheLaunch {
@@ -75,6 +142,8 @@ int decode_ring_bytes(int depth);
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream);
+hipError_t launch_fused_threshold(const FusedTopkLaunch &p, hipStream_t stream);
+hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream);
 hipError_t launch_kcache_insert(const KcacheLaunch &p, hipStream_t stream);
 
 } // namespace mqa

@@ -30,7 +30,9 @@
 //
 // Row reads are 16-byte loads, kUnroll per thread in flight: one workgroup
 // streams a whole row, so the bytes in flight per CU set its read rate.
+#include "device.h"
 #include "launch.h"
+#include "order_key.h"
 
 #include <atomic>
 
@@ -50,31 +52,24 @@ constexpr int kMaxCrowd = kSortCap / (kBucketMax + 1) + 1;  // crowded buckets a
 constexpr int kUnroll = 8;                  // 16-byte loads in flight per thread
 
 static_assert(kSample == 4 * kThreads, "the sample is four entries per thread");
+static_assert(kFusedSampleCols == kSample, "the fused sample fills one threshold sample");
 static_assert(kSortCap <= 16 * kThreads, "the sort holds every gathered entry");
 
-// Unsigned order == float order; 0 for -inf and NaN; -0.0 maps like +0.0.
-__device__ __forceinline__ uint32_t order_key(float v)
+// Raise a kernel's dynamic LDS limit once per device.
+hipError_t raise_lds_limit(const void *fn, int bytes, std::atomic<uint64_t> &raised)
 {
-    uint32_t u = __float_as_uint(v);
-    if (!(v == v) || v == -__builtin_inff())
-        return 0u;
-    if (u == 0x80000000u)
-        u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inverse of order_key on keys >= 0x00800000 (the key of -FLT_MAX): for such
-// a key t and any float v, order_key(v) >= t exactly when v >= key_value(t).
-__device__ __forceinline__ float key_value(uint32_t t)
-{
-    return __uint_as_float((t & 0x80000000u) ? (t & 0x7fffffffu) : ~t);
-}
-
-// Sort entry: key in the high word, ~column in the low word, so that a larger
-// entry ranks first (larger key, then smaller column).  0 is padding.
-__device__ __forceinline__ uint64_t entry(uint32_t key, int col)
-{
-    return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)col);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(raised.load() & bit)) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess)
+            return e;
+        raised.fetch_or(bit);
+    }
+    return hipSuccess;
 }
 
 struct TopkShared {
@@ -108,7 +103,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 // lane whose span holds b, and the wave then scans that span one digit per
 // lane.  Writes b, the new `above` and the bucket size to sh.bcast[0..2] (not
 // written when above + total < k), and the total to bcast[3].
-__device__ void find_threshold(TopkShared &sh, int nbins, int above, int k, int lane)
+template <class SH>
+__device__ void find_threshold(SH &sh, int nbins, int above, int k, int lane)
 {
     const int w = nbins / 64;
     const int hi = nbins - lane * w;  // exclusive upper digit of this lane's span
@@ -578,31 +574,21 @@ __device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, 
     }
 }
 
-// A key t0 such that, judging by kSample entries of the row (256 runs of 16
-// adjacent columns, evenly spaced), about 1.25 k entries plus a few standard
-// deviations are >= t0: the 24-bit prefix of the sample's ts-th largest key,
-// located by two 12-bit histograms.  0 when the sample holds fewer than ts
-// listable keys.  Needs cols > kSample.
-__device__ uint32_t sample_threshold(TopkShared &sh, const float *x, int cols, int k, int tid,
-                                     int lane, int wave)
+// The 24-bit prefix of the ts-th largest of the keys the block holds
+// (EPT per thread; 0 = not listable), located by two 12-bit histograms; 0
+// when fewer than ts keys are listable.
+template <int NT, int EPT, class SH>
+__device__ __forceinline__ uint32_t keys_threshold(SH &sh, const uint32_t (&samp)[EPT], int ts,
+                                                   int tid, int lane, int wave)
 {
-    const int pos = (int)(((int64_t)(tid >> 2) * cols / 256) & ~(int64_t)15) + 4 * (tid & 3);
-    float4 f;
-    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
-        f = *reinterpret_cast<const float4 *>(x + pos);
-    else
-        f = make_float4(x[pos], x[pos + 1], x[pos + 2], x[pos + 3]);
-    const uint32_t samp[4] = {order_key(f.x), order_key(f.y), order_key(f.z), order_key(f.w)};
-    for (int i = tid; i < kMaxBins; i += kThreads)
+    for (int i = tid; i < kMaxBins; i += NT)
         sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < EPT; ++s)
         if (samp[s] != 0u)
             atomicAdd(&sh.hist[samp[s] >> 20], 1u);
     __syncthreads();
-    const float m = (float)kSample * (float)k / (float)cols;
-    const int ts = (int)ceilf(1.25f * m + 3.0f * sqrtf(m) + 4.0f);
     if (wave == 0)
         find_threshold(sh, kMaxBins, 0, ts, lane);
     __syncthreads();
@@ -611,11 +597,11 @@ __device__ uint32_t sample_threshold(TopkShared &sh, const float *x, int cols, i
     const uint32_t b0 = (uint32_t)sh.bcast[0];
     const int above0 = sh.bcast[1];
     __syncthreads();  // hist and bcast are reused below
-    for (int i = tid; i < kMaxBins; i += kThreads)
+    for (int i = tid; i < kMaxBins; i += NT)
         sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < EPT; ++s)
         if (samp[s] != 0u && (samp[s] >> 20) == b0)
             atomicAdd(&sh.hist[(samp[s] >> 8) & 0xfffu], 1u);
     __syncthreads();
@@ -625,6 +611,45 @@ __device__ uint32_t sample_threshold(TopkShared &sh, const float *x, int cols, i
     const uint32_t t0 = (b0 << 20) | ((uint32_t)sh.bcast[0] << 8);
     __syncthreads();
     return t0 > 0u ? t0 : 1u;
+}
+
+// Survivor target of a sampled threshold: the ts-th largest of a sample
+// that holds m expected members of the top k leaves about 1.25 k entries of
+// the population at or above it, plus a few standard deviations.
+__device__ __forceinline__ int sample_rank(float m)
+{
+    return (int)ceilf(1.25f * m + 3.0f * sqrtf(m) + 4.0f);
+}
+
+// A key t0 such that, judging by kSample entries of the row (256 runs of 16
+// adjacent columns, evenly spaced), about 1.25 k entries plus a few standard
+// deviations are >= t0.  0 when the sample holds too few listable keys.
+// Needs cols > kSample.
+template <int NT, class SH>
+__device__ __forceinline__ uint32_t sample_threshold(SH &sh, const float *x, int cols, int k, int tid,
+                                                     int lane, int wave)
+{
+    // sample entries g = EPT tid .. EPT tid + EPT - 1: run g / 16, offset g % 16
+    constexpr int EPT = kSample / NT;
+    static_assert(EPT % 4 == 0 && 16 % EPT == 0, "whole float4 groups inside one run");
+    const int g = EPT * tid;
+    const int pos = (int)(((int64_t)(g / 16) * cols / 256) & ~(int64_t)15) + g % 16;
+    uint32_t samp[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+        const int q = pos + 4 * j;
+        float4 f;
+        if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
+            f = *reinterpret_cast<const float4 *>(x + q);
+        else
+            f = make_float4(x[q], x[q + 1], x[q + 2], x[q + 3]);
+        samp[4 * j + 0] = order_key(f.x);
+        samp[4 * j + 1] = order_key(f.y);
+        samp[4 * j + 2] = order_key(f.z);
+        samp[4 * j + 3] = order_key(f.w);
+    }
+    const int ts = sample_rank((float)kSample * (float)k / (float)cols);
+    return keys_threshold<NT, EPT>(sh, samp, ts, tid, lane, wave);
 }
 
 // Exact selection by radix passes (the path for any row the sampled
@@ -724,6 +749,30 @@ __device__ int radix_select(TopkShared &sh, const float *x, int cols, int k, int
     return k;
 }
 
+// Sort the n entries gathered in sh.buf (n <= kSortCap; they hold the row's
+// top min(n, k)) and write the row's k output columns.
+__device__ __forceinline__ void sort_and_write(TopkShared &sh, int n, int32_t *out, int k, int tid,
+                                               int lane, int wave)
+{
+    if (!bucket_sort(sh, n, tid, lane, wave)) {
+        // Many equal or clustered keys: bitonic sort of the smallest power of
+        // two >= n, padded with 0 (ranks last).
+        int n2 = 1;
+        while (n2 < n)
+            n2 <<= 1;
+        const int span = max(n2, 64 * E);
+        for (int i = n + tid; i < span; i += kThreads)
+            sh.buf[i] = 0ull;
+        __syncthreads();
+        sort_desc(sh, n2, tid, lane);
+    }
+    const uint64_t *order = sh.buf;
+
+    const int nsel = min(n, k);
+    for (int j = tid; j < k; j += kThreads)
+        out[j] = j < nsel ? (int32_t)(~(uint32_t)(order[j] & 0xffffffffull)) : -1;
+}
+
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ logits,
                                                         int32_t *__restrict__ indices, int cols,
                                                         int k)
@@ -751,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
         float4 first[kUnroll];
         if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
             load_batch(x, cols, tid, first);
-        const uint32_t t0 = sample_threshold(sh, x, cols, k, tid, lane, wave);
+        const uint32_t t0 = sample_threshold<kThreads>(sh, x, cols, k, tid, lane, wave);
         if (t0 != 0u) {
             // order_key(v) >= t0  <=>  v >= f0 (t0 raised to the smallest
             // listable key changes nothing and keeps f0 finite, so -inf and
@@ -768,45 +817,245 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
             n = radix_select(sh, x, cols, k, tid, lane, wave);
     }
     __syncthreads();
+    sort_and_write(sh, n, out, k, tid, lane, wave);
+}
 
-    if (!bucket_sort(sh, n, tid, lane, wave)) {
-        // Many equal or clustered keys: bitonic sort of the smallest power of
-        // two >= n, padded with 0 (ranks last).
-        int n2 = 1;
-        while (n2 < n)
-            n2 <<= 1;
-        const int span = max(n2, 64 * E);
-        for (int i = n + tid; i < span; i += kThreads)
-            sh.buf[i] = 0ull;
-        __syncthreads();
-        sort_desc(sh, n2, tid, lane);
+// ---- fused decode top-k -------------------------------------------------
+// The decode kernel's sample mode leaves kFusedSampleCols logits per row (-inf
+// outside the window); its filter mode then keeps, per row, every entry at or
+// above the row's threshold in per-workgroup segments.  The threshold comes
+// from the sample as in the one-row top-k.  The select step then has exactly
+// what the one-row filter would have kept, and sorts it the same way.  A row
+// it cannot resolve (the sample misjudged it) is recomputed in full by the
+// same workgroup: its logits into its own workspace segment, then the exact
+// radix select.  So the output equals the top-k of the logits call's output.
+
+// Listable positions of row r (p <= ctx - next_n + j, p < min(ctx, mml)).
+__device__ __forceinline__ int row_population(const int32_t *ctx_lens, int r, int next_n, int mml)
+{
+    const int b = r / next_n, j = r % next_n;
+    const int ctx = ctx_lens[b];
+    const int nvalid = max(min(ctx, mml), 0);
+    return max(0, min(ctx - next_n + j + 1, nvalid));
+}
+
+// The row-recompute inputs of the fused select (a kernel argument).
+struct FusedRowArgs {
+    uint64_t *entries;
+    int64_t ent_stride;
+    const int32_t *ctx_lens;
+    int next_n;
+    int mml;
+    const uint8_t *q;
+    const uint8_t *cache;
+    const float *weights;
+    const int32_t *tables;
+    int mbps;
+    int tiled;
+};
+
+struct ThresholdShared {
+    uint32_t hist[kMaxBins];
+    int bcast[4];
+    int listable;
+};
+
+constexpr int kThresholdThreads = kThreads;
+
+__global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
+    const float *__restrict__ sample, const int32_t *__restrict__ ctx_lens, int next_n, int mml,
+    int k, uint32_t *__restrict__ threshold)
+{
+    __shared__ ThresholdShared sh;
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    const int pop = row_population(ctx_lens, r, next_n, mml);
+    if (pop <= kSortCap) {
+        // short row: keep every listable entry (key >= 1)
+        if (tid == 0)
+            threshold[r] = 1u;
+        return;
     }
-    const uint64_t *order = sh.buf;
+    constexpr int EPT = kFusedSampleCols / kThresholdThreads;
+    const float *x = sample + (int64_t)r * kFusedSampleCols + EPT * tid;
+    uint32_t samp[EPT];
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < EPT; j += 4) {
+        const float4 f = *reinterpret_cast<const float4 *>(x + j);
+        samp[j + 0] = order_key(f.x);
+        samp[j + 1] = order_key(f.y);
+        samp[j + 2] = order_key(f.z);
+        samp[j + 3] = order_key(f.w);
+        mine += (samp[j] != 0u) + (samp[j + 1] != 0u) + (samp[j + 2] != 0u) + (samp[j + 3] != 0u);
+    }
+    if (tid == 0)
+        sh.listable = 0;
+    __syncthreads();
+    atomicAdd(&sh.listable, mine);
+    __syncthreads();
+    const int listable = sh.listable;
+    const int ts = sample_rank((float)listable * (float)k / (float)pop);
+    uint32_t t0 = 0u;  // 0: no threshold (the row is recomputed in full)
+    if (ts <= listable)
+        t0 = keys_threshold<kThresholdThreads, EPT>(sh, samp, ts, tid, tid & 63, tid >> 6);
+    if (tid == 0)
+        threshold[r] = t0;
+}
 
-    const int nsel = min(n, k);
-    for (int j = tid; j < k; j += kThreads)
-        out[j] = j < nsel ? (int32_t)(~(uint32_t)(order[j] & 0xffffffffull)) : -1;
+// Row r's logits (the decode call's values, -inf outside the window) into
+// x[0, mml): the workgroup's waves take the row's 64-token steps in turn and
+// compute them with the decode kernel's contraction and epilogue (one row per
+// wave, K straight from the cache), so every value equals the decode call's.
+__device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, int r, int tid,
+                                              int lane, int wave)
+{
+    const int b = r / ra.next_n, j = r % ra.next_n;
+    const int ctx = ra.ctx_lens[b];
+    const int nvalid = max(min(ctx, ra.mml), 0);
+    const int nsteps = (nvalid + kStep - 1) / kStep;
+    const int bound = ctx - ra.next_n + j;  // inclusive
+    const int t = lane & 31, g = lane >> 5;
+    Frag q[1][1];
+    Weights16 w[1][1];
+    load_frag(q[0][0], ra.q + (int64_t)r * (kHeads * kDim) + t * kDim, lane);
+    load_weights(w[0][0], ra.weights + (int64_t)r * kHeads, lane);
+    const int32_t *table = ra.tables + (int64_t)b * ra.mbps;
+    const float ninf = -__builtin_inff();
+    for (int st = wave; st < nsteps; st += kWaves) {
+        const uint8_t *blk = ra.cache + (int64_t)table[st] * kBlockBytes;
+        KStep k;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int slot = kTile * h + t;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int u = 2 * c + g;  // 16-byte granule of the row
+                const int off = ra.tiled ? (slot >> 4) * (16 * kDim) + u * 256 + (slot & 15) * 16
+                                         : slot * kDim + u * 16;
+                k.t[h].c[c] = *reinterpret_cast<const i32x4 *>(blk + off);
+            }
+            k.sc[h] = *reinterpret_cast<const float *>(blk + kBlock * kDim + 4 * slot);
+        }
+        float tot[2][1];
+        step_scores<1, 1>(k, q, w, tot);
+        if (lane < 32) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int p = st * kStep + h * kTile + t;
+                if (p < ra.mml)
+                    x[p] = p <= bound ? tot[h][0] : ninf;
+            }
+        }
+    }
+    for (int p = nsteps * kStep + tid; p < ra.mml; p += kThreads)
+        x[p] = ninf;
+}
+
+__global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
+                                                                const int *__restrict__ counts,
+                                                                int split, int k,
+                                                                int32_t *__restrict__ indices,
+                                                                int *__restrict__ recomputed)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
+    TopkShared &sh = *reinterpret_cast<TopkShared *>(topk_lds);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = blockIdx.x;
+    const int b = r / ra.next_n;
+    const int pop = row_population(ra.ctx_lens, r, ra.next_n, ra.mml);
+    const int nvalid = max(min(ra.ctx_lens[b], ra.mml), 0);
+    const int nsteps = (nvalid + 63) / 64;
+    const int *cnt = counts + (int64_t)r * split;
+    uint64_t *row = ra.entries + (int64_t)r * ra.ent_stride;
+    int32_t *out = indices + (int64_t)r * k;
+
+    // exclusive prefix of the segment counts (split <= kThreads) in sh.hist
+    const int c = tid < split ? cnt[tid] : 0;
+    const int incl = wave_inclusive_scan(c, lane);
+    if (lane == 63)
+        sh.wave_total[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int v = 0; v < kWaves; ++v) {
+        before += v < wave ? sh.wave_total[v] : 0;
+        total += sh.wave_total[v];
+    }
+    if (tid < split)
+        sh.hist[tid] = (uint32_t)(before + incl - c);
+    // Every entry at or above the threshold survived; if at least k did (or
+    // every listable one did), they hold the row's top k.
+    const bool ok = (total >= k || total == pop) && total <= kSortCap;
+    if (tid == 0)
+        recomputed[r] = ok ? 0 : 1;
+    __syncthreads();
+    int n;
+    if (ok) {  // uniform
+        // segment s starts at the first column of the filter workgroup s
+        for (int sgm = wave; sgm < split; sgm += kWaves) {
+            const int m = cnt[sgm];
+            const int64_t col0 = (int64_t)nsteps * sgm / split * 64;
+            const int dst = (int)sh.hist[sgm];
+            for (int i = lane; i < m; i += 64)
+                sh.buf[dst + i] = row[col0 + i];
+        }
+        n = total;
+    } else {
+        // the row's own segment region (>= mml floats) now holds its logits
+        float *x = reinterpret_cast<float *>(row);
+        recompute_row(x, ra, r, tid, lane, wave);
+        __threadfence_block();
+        __syncthreads();
+        n = radix_select(sh, x, ra.mml, k, tid, lane, wave);
+    }
+    __syncthreads();
+    sort_and_write(sh, n, out, k, tid, lane, wave);
 }
 
 } // namespace
 
-hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream)
+hipError_t launch_fused_threshold(const FusedTopkLaunch &p, hipStream_t stream)
 {
-    // The LDS block (~80 KiB) is above the default dynamic limit; raise it
-    // once per device.
+    hipLaunchKernelGGL(fused_threshold_kernel, dim3(p.batch * p.next_n), dim3(kThresholdThreads), 0,
+                       stream, p.ws->sample, p.context_lens, p.next_n, p.mml, p.k, p.ws->threshold);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream)
+{
     static std::atomic<uint64_t> raised{0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&fused_select_kernel),
+                                   (int)sizeof(TopkShared), raised);
     if (e != hipSuccess)
         return e;
-    const uint64_t bit = 1ull << (dev & 63);
-    if (!(raised.load() & bit)) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(TopkShared));
-        if (e != hipSuccess)
-            return e;
-        raised.fetch_or(bit);
-    }
+    FusedRowArgs ra;
+    ra.entries = p.ws->entries;
+    ra.ent_stride = p.ws->ent_stride;
+    ra.ctx_lens = p.context_lens;
+    ra.next_n = p.next_n;
+    ra.mml = p.mml;
+    ra.q = p.q;
+    ra.cache = p.cache;
+    ra.weights = p.weights;
+    ra.tables = p.block_tables;
+    ra.mbps = p.max_blocks_per_seq;
+    ra.tiled = p.tiled;
+    hipLaunchKernelGGL(fused_select_kernel, dim3(p.batch * p.next_n), dim3(kThreads),
+                       sizeof(TopkShared), stream, ra, p.ws->counts, p.split, p.k, p.indices,
+                       p.ws->recomputed);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream)
+{
+    // The LDS block (~146 KiB) is above the default dynamic limit.
+    static std::atomic<uint64_t> raised{0};
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&topk_kernel),
+                                   (int)sizeof(TopkShared), raised);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(topk_kernel, dim3(p.rows), dim3(kThreads), sizeof(TopkShared), stream,
                        p.logits, p.indices, p.cols, p.k);
     return hipGetLastError();

@@ -157,6 +157,46 @@ def test_topk_validation(lib):
     assert "aligned" in mqa.last_error()
 
 
+def test_fused_topk_workspace_size(lib):
+    ws = lib.paged_mqa_topk_workspace_size
+    big = ws(16, 6, 131072)
+    assert 96 * 131072 * 8 <= big <= 96 * 131072 * 8 + 96 * 1024 * 4 + 96 * 4096 * 4 + 96 * 8 + 5 * 256
+    assert ws(0, 6, 131072) == 0 and ws(16, 0, 131072) == 0 and ws(16, 9, 131072) == 0
+    assert ws(16, 6, 0) == 0
+    assert ws(1, 1, 1) > 0
+    assert mqa.paged_mqa_topk_workspace_size(16, 6, 131072) == big
+
+
+def _fused(lib, ptrs, B=2, nn=1, H=32, D=128, bs=64, nb=4, mbps=2, mml=128, k=16, ws=None,
+           wsb=0, tun=None, layout=0):
+    return lib.paged_mqa_topk_decode(*ptrs, B, nn, H, D, bs, layout, nb, mbps, mml, k, ws, wsb,
+                                     tun, None)
+
+
+def test_fused_topk_validation(lib):
+    nulls = [None] * 6
+    E = mqa._native
+    assert _fused(lib, nulls, k=0) == E.MQA_ERR_INVALID_ARG
+    assert "k must be" in mqa.last_error()
+    assert _fused(lib, nulls, k=2049) == E.MQA_ERR_INVALID_ARG
+    assert _fused(lib, nulls, H=64) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, bs=16) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, bs=1) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, D=64) == E.MQA_ERR_UNSUPPORTED
+    bad = E.Tunables(ring_depth=4)
+    assert _fused(lib, nulls, tun=ctypes.byref(bad)) == E.MQA_ERR_INVALID_ARG
+    assert _fused(lib, nulls, B=0) == 0          # nothing to do, nothing dereferenced
+    assert _fused(lib, nulls, mml=0) == 0
+    assert _fused(lib, nulls) == E.MQA_ERR_INVALID_ARG
+    assert "NULL" in mqa.last_error()
+    need = lib.paged_mqa_topk_workspace_size(2, 1, 128)
+    fake = [P(0x10000)] * 6  # never dereferenced: rejected before the device is touched
+    assert _fused(lib, fake, ws=P(0x20080), wsb=need) == E.MQA_ERR_INVALID_ARG
+    assert "aligned" in mqa.last_error()
+    assert _fused(lib, fake, ws=P(0x20000), wsb=need - 1) == E.MQA_ERR_INVALID_ARG
+    assert "workspace" in mqa.last_error()
+
+
 def test_kcache_validation(lib):
     f = lib.mqa_kcache_quantize_insert
     assert f(None, 0, None, None, -1, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG

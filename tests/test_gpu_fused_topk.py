@@ -1,0 +1,169 @@
+"""GPU parity of the fused decode top-k (paged_mqa_topk_decode).
+
+Its output is defined as the top-k of the decode logits, so it must equal,
+bit for bit, the one-row top-k (mqa_topk_indices, itself checked bit-exactly
+against the oracle's top-k) of the logits the decode call writes (checked
+against the oracle's logits).  On integer-valued inputs the logits are exact
+in fp32, so there the fused indices must also equal the oracle's top-k of the
+oracle's own logits.  Cases reach every path of the fused call: short rows
+(every listable entry kept), the sampled threshold, ragged and empty windows,
+the preshuffled cache, and rows the sample misjudges (too few or too many
+kept entries), which are recomputed in full.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.topk import topk_indices as oracle_topk
+from sparse_attention_indexer_scaled_amd import Tunables, _native, inputs
+from tests.gpu_util import decode_device_inputs, lib, run_decode, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    lib()
+
+
+def fused(d, k, tun=None, dv=None):
+    dv = dv or decode_device_inputs(d)
+    need = _native.paged_mqa_topk_workspace_size(d.B, d.next_n, d.max_model_len)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")  # contents must not matter
+    out = torch.full((d.B * d.next_n, k), -7, dtype=torch.int32, device="cuda")
+    _native.paged_mqa_topk_decode(dv["q"], dv["cache"], dv["w"], dv["ctx"], dv["bt"],
+                                  d.max_model_len, k, kv_block_size=d.block_size, indices=out,
+                                  workspace=ws, tunables=tun, preshuffle=d.preshuffle)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def unfused(d, k, dv=None):
+    logits = torch.from_numpy(np.ascontiguousarray(run_decode(d, dv=dv))).cuda()
+    out = _native.topk_indices(logits, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def assert_same(got, want, tag):
+    if not np.array_equal(got, want):
+        bad = np.nonzero((got != want).any(axis=1))[0]
+        r = int(bad[0])
+        j = int(np.nonzero(got[r] != want[r])[0][0])
+        raise AssertionError("%s: %d rows differ; row %d first at %d: fused %s unfused %s" % (
+            tag, bad.size, r, j, got[r, j:j + 4], want[r, j:j + 4]))
+
+
+CASES = [
+    (3, 2, [700, 130, 3000], 3072),         # short rows: every listable entry kept
+    (2, 6, [20000, 7], 20001),              # a long row and an almost empty one
+    (4, 1, [0, 15, 9000, 40000], 40960),    # empty, tiny, just past the keep-all size, long
+    (2, 3, [65536, 65536], 65536),          # the sampled threshold on long rows
+    (2, 8, [131072, 100000], 131072),
+]
+
+
+@pytest.mark.parametrize("B,next_n,ctx,mml", CASES, ids=["B%d-nn%d-mml%d" % (b, n, m)
+                                                         for b, n, _, m in CASES])
+def test_fused_equals_topk_of_logits(B, next_n, ctx, mml):
+    d = inputs.make_decode(B, next_n, ctx, mml, seed=900 + mml % 97, poison=True)
+    dv = decode_device_inputs(d)
+    for k in (1, 64, 512, 2048):
+        say("fused topk B=%d next_n=%d ctx=%s k=%d" % (B, next_n, ctx, k))
+        assert_same(fused(d, k, dv=dv), unfused(d, k, dv=dv), "ctx=%s k=%d" % (ctx, k))
+
+
+def test_fused_headline_shape():
+    """The benchmark's shape: 16 sequences of 131072, next_n 6."""
+    d = inputs.make_config(2)
+    dv = decode_device_inputs(d)
+    for k in (512, 2048):
+        say("fused topk headline k=%d" % k)
+        assert_same(fused(d, k, dv=dv), unfused(d, k, dv=dv), "headline k=%d" % k)
+
+
+def test_fused_preshuffled_cache_and_tunables():
+    d = inputs.make_decode(2, 4, [30000, 12000], 30016, seed=910, preshuffle=True, poison=True)
+    dv = decode_device_inputs(d)
+    want = unfused(d, 2048, dv=dv)
+    for tun in (None, Tunables(split_kv=1), Tunables(rows_per_block=1, split_kv=37),
+                Tunables(rows_per_block=4, split_kv=300)):
+        say("fused topk preshuffled tun=%s" % (None if tun is None else
+                                               [getattr(tun, f) for f, _ in Tunables._fields_]))
+        assert_same(fused(d, 2048, tun=tun, dv=dv), want, "preshuffled")
+
+
+def _integer_decode(B, next_n, ctx, mml, seed):
+    """Integer fp8 values in [-8, 8] and power-of-two weights and scales:
+    every logit is exact in fp32, whatever the accumulation order."""
+    rng = np.random.default_rng(seed)
+    d = inputs.make_decode(B, next_n, ctx, mml, seed=seed, poison=True)
+    d.q = inputs.to_fp8_bytes(rng.integers(-8, 9, d.q.shape).astype(np.float32))
+    d.weights = (rng.choice([-1, 1], d.weights.shape) *
+                 2.0 ** -rng.integers(0, 4, d.weights.shape)).astype(np.float32)
+    kview, sview = inputs.cache_views(d.kv_cache, 64, 128)
+    used = d.num_blocks - 1  # the last block is the poison block
+    kview[:used] = inputs.to_fp8_bytes(rng.integers(-8, 9, kview[:used].shape).astype(np.float32))
+    sview[:used] = rng.choice([0.5, 1.0, 2.0], sview[:used].shape).astype(np.float32)
+    return d
+
+
+def test_fused_integer_inputs_match_the_oracle():
+    d = _integer_decode(2, 3, [20000, 9500], 20032, seed=920)
+    ref = oracle.decode(d.q, d.kv_cache, d.weights, d.context_lens, d.block_tables,
+                        d.max_model_len, 64).astype(np.float32)
+    for k in (100, 2048):
+        say("fused topk integer inputs k=%d" % k)
+        assert_same(fused(d, k), oracle_topk(ref, k), "integer k=%d" % k)
+
+
+def _sampled_steps(nsteps):
+    """Steps the sampling decode computes (16 runs of 4 evenly spaced steps)."""
+    span = max(nsteps - 4, 0)
+    steps = set()
+    for s in range(16):
+        st0 = span * s // 15
+        steps.update(range(st0, min(st0 + 4, nsteps)))
+    return sorted(steps)
+
+
+def _one_hot_logits(d, high_positions):
+    """Cache and queries such that the logit is exactly 1 at high_positions
+    (K = 1.0 in dim 0, every head's Q = 1.0 there, weights 1/32) and exactly
+    0 at every other position of the window."""
+    d.q[:] = 0
+    d.q[..., 0] = 0x38  # 1.0
+    d.weights[:] = np.float32(1.0 / 32)
+    kview, sview = inputs.cache_views(d.kv_cache, 64, 128)
+    used = d.num_blocks - 1
+    kview[:used] = 0
+    sview[:used] = 1.0
+    for b, pos in high_positions.items():
+        blocks = d.block_tables[b, np.asarray(pos) // 64]
+        kview[blocks, np.asarray(pos) % 64, 0] = 0x38
+    return d
+
+
+def test_fused_rows_the_sample_misjudges():
+    """Row 0: 1000 positions at logit 1, all inside the sample, the rest 0: the
+    sampled threshold (1) keeps only 1000 < k entries.  Row 1: every logit 0:
+    the threshold keeps the whole row, more than can be sorted at once.  Both
+    are recomputed in full; the output must still be the exact top-k (ties at
+    0 by column)."""
+    ctx = 65536
+    d = inputs.make_decode(2, 1, [ctx, ctx], ctx, seed=930, poison=True)
+    sampled = np.concatenate([np.arange(64 * s, 64 * s + 64) for s in _sampled_steps(ctx // 64)])
+    high = np.sort(np.random.default_rng(931).choice(sampled, 1000, replace=False))
+    d = _one_hot_logits(d, {0: high})
+    for k in (2048, 1000, 999):
+        say("fused topk misjudged rows k=%d" % k)
+        got = fused(d, k)
+        assert_same(got, unfused(d, k), "misjudged k=%d" % k)
+        if k == 2048:
+            assert np.array_equal(got[0, :1000], high)
+            assert np.array_equal(got[1], np.arange(2048))
