@@ -520,6 +520,13 @@ def write_counter_profile(workload_name, kernel_part, dirs, command):
     if "SQ_INSTS_VALU_MFMA_MOPS_F8" in avg:
         # one MOPS unit is 512 flops
         derived["mfma_fp8_flops"] = int(avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512)
+    hit, miss = avg.get("TCC_HIT_sum"), avg.get("TCC_MISS_sum")
+    if hit is not None and miss is not None and hit + miss > 0:
+        derived["l2_hit_frac"] = round(hit / (hit + miss), 4)
+    if "SQ_INSTS_LDS" in avg:
+        derived["lds_insts"] = int(avg["SQ_INSTS_LDS"])
+    if "SQ_WAVES" in avg:
+        derived["waves"] = int(avg["SQ_WAVES"])
     out["derived"] = derived
     os.makedirs(PROFILE_DIR, exist_ok=True)
     path = os.path.join(PROFILE_DIR, "%s_counters.json" % workload_name)
