@@ -31,6 +31,10 @@
 // by the same waves.  A position is selected by an integer compare, never by
 // arithmetic, so cache slots past the context (which may hold NaN bytes)
 // cannot reach an output.
+//
+// The same kernel serves the fused decode top-k in two more modes (see
+// DecodeMode): a sample of each sequence's steps, and a filter that keeps
+// only the entries at or above each row's threshold instead of storing logits.
 #include "device.h"
 #include "launch.h"
 #include "order_key.h"
