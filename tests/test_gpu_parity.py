@@ -324,3 +324,28 @@ def test_empty_problems_are_noops():
                                   torch.zeros((0, 1), dtype=torch.int32, device="cuda"), 64)
     assert out.shape == (0, 64)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# large sizes
+# ---------------------------------------------------------------------------
+
+
+def test_decode_max_model_len_one_million():
+    """max_model_len 1048576 (the long-context setting the issue page about
+    next_n tiling measures with) and contexts far shorter: the -inf fill
+    covers almost every row, every window is exact."""
+    d = inputs.make_decode(2, 2, [131072, 5000], 1048576, seed=420, poison=True)
+    say("decode mml=1048576")
+    out = run_decode(d)
+    ref, mag, _ = oracle_decode(d)
+    assert_parity(out, ref, mag, "decode_mml1M")
+
+
+def test_prefill_long_rows_few_queries():
+    """A handful of query rows over 131072 columns (large N, tiny M)."""
+    p = inputs.make_prefill(8, 131072, seed=421, windows="causal")
+    say("prefill M8 N131072")
+    out = run_prefill(p)
+    ref, mag = oracle_prefill(p)
+    assert_parity(out, ref, mag, "prefill_M8_N131072")
