@@ -5,12 +5,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -38,10 +38,10 @@ int ok()
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// gfx950 check for the current device, cached per device id.
+// gfx950 check for the current device, cached per device id (threads may race
+// to fill an entry; they store the same value).
 constexpr int kMaxDevices = 64;
-int g_arch_ok[kMaxDevices]; // 0 unknown, 1 gfx950, -1 other
-std::mutex g_arch_mu;
+std::atomic<int> g_arch_ok[kMaxDevices]; // 0 unknown, 1 gfx950, -1 other
 
 int current_device_is_gfx950(int *dev_out)
 {
@@ -52,18 +52,19 @@ int current_device_is_gfx950(int *dev_out)
     }
     if (dev_out)
         *dev_out = dev;
-    if (dev < kMaxDevices && g_arch_ok[dev] != 0)
-        return g_arch_ok[dev] > 0 ? 1 : 0;
+    if (dev < kMaxDevices) {
+        const int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (known != 0)
+            return known > 0 ? 1 : 0;
+    }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
         (void)hipGetLastError();
         return -1;
     }
     const int is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
-    if (dev < kMaxDevices) {
-        std::lock_guard<std::mutex> lk(g_arch_mu);
-        g_arch_ok[dev] = is950 ? 1 : -1;
-    }
+    if (dev < kMaxDevices)
+        g_arch_ok[dev].store(is950 ? 1 : -1, std::memory_order_relaxed);
     return is950;
 }
 
