@@ -574,8 +574,9 @@ def main():
         write_kernel_stats(args.write_kernel_stats[0], args.write_kernel_stats[1], args.profile_command)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the op needs no exchange between GPUs; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the op shards by sequence or row block "
+              "with no exchange between GPUs, so the one-GPU figure is the measurement",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "needs a HIP device"

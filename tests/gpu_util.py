@@ -24,7 +24,8 @@ import oracle
 from sparse_attention_indexer_scaled_amd import _native
 from tests.util import calc_diff, mask_equal
 
-OUT_DIR = os.environ.get("MQA_FAIL_DIR", "gpurun_out")
+OUT_DIR = os.environ.get("MQA_FAIL_DIR",
+                         os.path.join(__import__("tempfile").gettempdir(), "mqa_failures"))
 REL_TOL = 1e-5
 CALC_DIFF_GATE = 1e-3
 
