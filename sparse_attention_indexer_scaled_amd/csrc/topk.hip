@@ -368,9 +368,18 @@ __device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int 
         const int st = b > 0 ? (int)sh.hist[b - 1] : 0;
         if (end - st > kBucketMax)
             continue;  // ranked below by the whole block
+        // eight reads in flight per round (a dependent read per entry would
+        // wait out the LDS latency each time)
         int r = 0;
-        for (int j = st; j < end; ++j)
-            r += sh.sorted[j] > e;
+        for (int j = st; j < end; j += 8) {
+            uint64_t o[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                o[q] = sh.sorted[min(j + q, end - 1)];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                r += (j + q < end) && o[q] > e;
+        }
         sh.buf[st + r] = e;
     }
     __syncthreads();
