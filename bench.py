@@ -378,7 +378,8 @@ PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles
 
 
 KERNEL_SOURCES = {
-    "decode_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "decode.hip"),
+    "decode_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "decode_kernel.h",
+                      "decode.hip"),
     "prefill_kernel": ("device.h", "launch.h", "api.cpp", "prefill.hip"),
     "topk_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "topk.hip"),
     "kcache_insert_kernel": ("device.h", "launch.h", "api.cpp", "kcache.hip"),

@@ -223,11 +223,13 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  * k (the sample misjudged it) is recomputed in full by its select workgroup
  * (its logits into its workspace segment, then an exact radix select), so the
  * output is exact for every input; such rows only take longer.
- * Supported: num_heads 32, head_dim 128, kv_block_size 64 (either kv_layout),
- * ring_depth tunable 0 or 3, a KV split of at most 1024.  Errors as for
- * paged_mqa_logits_decode, plus: k out of range, NULL or misaligned indices or
- * workspace, a workspace smaller than asked for -> MQA_ERR_INVALID_ARG; other
- * head counts or block sizes -> MQA_ERR_UNSUPPORTED.
+ * Supported: every head count, block size and kv_layout that
+ * paged_mqa_logits_decode takes; the ring_depth tunable 0 or the logits
+ * call's default (3 for 64-token blocks at 32 heads, else 4); a KV split of
+ * at most 1024.  Errors as for paged_mqa_logits_decode (a shape outside its
+ * gate -> MQA_ERR_UNSUPPORTED, checked first), plus: k out of range, another
+ * ring_depth, NULL or misaligned indices or workspace, a workspace smaller
+ * than asked for -> MQA_ERR_INVALID_ARG.
  */
 int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *weights,
                           const int32_t *context_lens, const int32_t *block_tables,

@@ -356,11 +356,16 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
 {
     if (k < 1 || k > mqa::kMaxTopK)
         return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
-    if (tun && tun->ring_depth != 0 && tun->ring_depth != 3)
-        return fail(MQA_ERR_INVALID_ARG, "the fused top-k runs the default ring depth (0 or 3)");
-    if (num_heads != 32 || head_dim != 128 || kv_block_size != 64)
-        return fail(MQA_ERR_UNSUPPORTED, "the fused top-k supports num_heads 32, head_dim 128 and "
-                    "kv_block_size 64 (got %d, %d, %d)", num_heads, head_dim, kv_block_size);
+    if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
+        return fail(MQA_ERR_UNSUPPORTED,
+                    "the fused top-k takes the decode's shapes: num_heads=32 with kv_block_size 1, "
+                    "16, 64 or 128, or num_heads 64 / 128 with kv_block_size 64; head_dim=128 "
+                    "(got %d, %d, %d)", num_heads, head_dim, kv_block_size);
+    // the sample and filter modes are built for the logits call's default ring
+    const int depth = (kv_block_size == 64 && num_heads == 32) ? 3 : 4;
+    if (tun && tun->ring_depth != 0 && tun->ring_depth != depth)
+        return fail(MQA_ERR_INVALID_ARG, "the fused top-k runs the default ring depth (0 or %d "
+                    "for this shape)", depth);
     if (batch > 0 && max_model_len > 0 && next_n >= 1 && next_n <= 8) {
         if (!indices || !workspace)
             return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
@@ -383,12 +388,13 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
     if (p.split_kv > mqa::kFusedMaxSplit)
         return fail(MQA_ERR_INVALID_ARG, "the fused top-k takes split_kv <= %d (got %d)",
                     mqa::kFusedMaxSplit, p.split_kv);
-    p.depth = 3;  // the sample and filter modes are built for the 3-step ring
+    p.depth = depth;
     const int rows = batch * next_n;
     const mqa::FusedWorkspace w = mqa::fused_workspace(workspace, rows, max_model_len);
     mqa::FusedTopkLaunch f{&w,      context_lens, indices, batch,   next_n,
                            max_model_len, k,   p.split_kv, q_fp8, kv_cache,
-                           weights, block_tables, max_blocks_per_seq, p.tiled};
+                           weights, block_tables, max_blocks_per_seq, p.tiled,
+                           kv_block_size, p.head_tiles};
     hipError_t e;
     // 1. the sample: kFusedSampleChunks runs of steps per sequence
     mqa::DecodeLaunch ps = p;

@@ -1,0 +1,621 @@
+// Paged decode kernel template (gfx950), shared by the logits call (decode.hip)
+// and the fused top-k's sample and filter modes (decode_fused.hip).
+//
+// What it computes (aiter PR 5047 page, "Motivation" and "Technical Details"):
+// row j of sequence b gets  sum_h relu(<Q[b,j,h,:], K[p,:]>) * w[b,j,h] * scale[p]
+// for every cached position p <= ctx_b - next_n + j, K and its per-token scale
+// read from a paged cache through the block table; -inf elsewhere (fused fill).
+//
+// Work decomposition.  A workgroup owns one (sequence b, KV split s) and walks
+// the split's 64-token steps (one cache block each) in order.  Its G waves are
+// row groups: wave g holds rows [g R, g R + R) of the sequence's next_n rows
+// (Q: 16 VGPR per row, head weights: 16 VGPR per row, for the wave's whole
+// life).  All rows of the sequence share ONE K stream (both pages, "Technical
+// Details": rows share one K stream; the next_n-tiling issue page asks for
+// next_n folded into the tile rather than into the program count):
+//
+//   - K and scales travel HBM -> LDS by direct loads (global_load_lds, no
+//     VGPRs) into a ring of D slots, each slot one cache block (8 KiB of K in a
+//     bank-conflict-free order + 256 B of scales).  Step k+D-1 is requested
+//     while step k computes, so D-1 blocks per workgroup are always in flight
+//     and the ring, not the register file, holds the bytes in flight.
+//   - The G waves split each block's nine load instructions between them,
+//     then every wave reads the whole block from LDS (ds_read_b128) into the
+//     MFMA operand layout.  One s_barrier per step publishes the block to all
+//     waves and retires the slot the next request overwrites.
+//   - Per 32-token tile and row: two fp8 MFMAs, the in-lane relu.weight sum
+//     over 16 heads, one permlane32 swap + add per row pair, kv_scale once per
+//     column (the hoist: kv_scale >= 0, relu positive-homogeneous).
+//   - A step's results are stored one step later, so the stores retire while
+//     the next step computes.
+// Positions past the sequence's context up to max_model_len are written -inf
+// by the same waves.  A position is selected by an integer compare, never by
+// arithmetic, so cache slots past the context (which may hold NaN bytes)
+// cannot reach an output.
+//
+// The same kernel serves the fused decode top-k in two more modes (see
+// DecodeMode): a sample of each sequence's steps, and a filter that keeps
+// only the entries at or above each row's threshold instead of storing logits.
+#pragma once
+
+#include "device.h"
+#include "launch.h"
+#include "order_key.h"
+
+namespace mqa {
+namespace {
+
+
+constexpr int kSlotBytes = kBlockBytes;  // ring slot: one 64-token step, K rows + scales
+constexpr int kSampleChunks = kFusedSampleChunks;
+constexpr int kSampleSteps = kFusedSampleSteps;
+constexpr int kSampleCols = kFusedSampleCols;
+
+// LDS bytes of a workgroup's ring (and, for per-token blocks, its table
+// ring).
+template <int D, int BS>
+constexpr int ring_lds_bytes()
+{
+    return D * kSlotBytes + (BS == 1 ? (2 * D - 2) * kStep * 4 : 0);
+}
+constexpr int kChunks = kDim * kBlock / 1024 + 1;  // 8 x 1 KiB of K + 1 x 256 B of scales
+
+// Sizes and launch shape; the pointers are separate __restrict__ kernel
+// arguments so the compiler may read the block table with scalar loads.
+struct DecodeArgs {
+    int mml;
+    int next_n;
+    int mbps;
+    int clean;
+    int groups;
+    int split;
+    int tiled;  // K rows of a block in the preshuffled (16,16) order
+    // Fused top-k (see the kernel's modes; unused by the plain logits call):
+    float *sample;                // sample mode: [rows][kSampleCols]
+    const uint32_t *threshold;    // filter mode: [rows] order-key thresholds
+    uint64_t *entries;            // filter mode: [rows][ent_stride]
+    int *counts;                  // filter mode: [rows][split]
+    int64_t ent_stride;
+};
+
+// Kernel modes.  kLogits: the op's output.  The fused top-k adds two:
+// kSample computes kSampleChunks evenly spaced runs of kSampleSteps steps of
+// each sequence (the sample its thresholds are drawn from) into a small
+// buffer, -inf outside the windows; kFilter computes every step like kLogits
+// but, instead of storing the logits, appends the (key, column) entries of
+// each row at or above the row's threshold to the workgroup's own segment of
+// the row (it starts at the workgroup's first column, so it can never
+// overflow), and stores their count.
+enum DecodeMode { kLogits = 0, kSample = 1, kFilter = 2 };
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Cache-policy bits of the global->LDS loads: nt (non-temporal).  Every cache
+// byte is read once per call, so the loads are marked streaming; measured on
+// MI355X this is worth about 10% on the long-context decode.
+constexpr int kStreamHint = 2;
+
+// Where the 64 tokens of one step come from in a cache of BS-token blocks,
+// and how they are requested into a ring slot.  The slot layout is the same
+// for every block size (see read_block): 8 x 1 KiB chunks of K rows, then the
+// 64 scales.  A global_load_lds instruction writes lane i's 16 bytes at
+// slot + 1024 c + 16 i, so the lane -> granule assignment decides the LDS
+// layout: position i of chunk c holds granule q = i ^ (8 (c & 1)) of the
+// chunk, where q = 8 u + tau is 16-byte granule u of token 8c + tau.  Odd
+// chunks swap the two 128-byte halves of each 256-byte row, so that one
+// 16-lane pass of ds_read_b128, which reads two neighbouring chunks, covers
+// all 64 LDS banks once.  Wave g of G issues K chunks g, g + G, ... and the
+// last wave also the scales, so every wave issues at least kChunks / G loads
+// per step.
+//
+// Blocks of 16 or more tokens hold whole 8-token chunks, so each chunk is one
+// coalesced 1 KiB read; the step's table entries (64 / BS of them, or one
+// entry covering several steps) are read with scalar loads.
+//
+// Such blocks may also hold their K rows in the preshuffled (16,16) order
+// (the 64-token pairing on the aiter PR 5047 page, "Technical Details"): the
+// slots in groups of 16, each group storing 16-byte granule u of its 16 rows
+// (row by row) before granule u + 1, so granule u of block row r sits at
+// (r / 16) 2048 + 256 u + 16 (r % 16).  Only the source addresses change: a
+// chunk's 64 granules are then eight 128-byte runs, and the two chunks of a
+// 16-row group read one contiguous 2 KiB; the ring slot is filled exactly as
+// from a slot-major block.
+// The block pointers of one step (one per table entry the step touches).
+template <int N>
+struct StepBlocks {
+    const uint8_t *p[N];
+};
+
+constexpr int entries_per_step(int bs) { return bs >= kStep ? 1 : kStep / bs; }
+
+template <int BS>
+struct Gather {
+    static_assert(BS == 16 || BS == 64 || BS == 128, "block sizes with whole chunks");
+    static constexpr int kEntries = entries_per_step(BS);        // table entries per step
+    static constexpr int64_t kBytes = (int64_t)BS * (kDim + 4);  // bytes per block
+
+    struct Src {
+        StepBlocks<kEntries> blk;
+        int off;  // first token of the step within its block (BS > 64)
+    };
+
+    // last: index of the sequence's last table entry that holds a token of
+    // the window.  Entries past it are never read (they may be padding): a
+    // step that ends beyond the context reuses the last entry, whose data
+    // never reaches an output.
+    __device__ static __forceinline__ Src fetch(const uint8_t *cache, const int32_t *table, int st,
+                                                int last)
+    {
+        Src src;
+        if (BS >= kStep) {
+            const int tok = st * kStep;
+            src.blk.p[0] = cache + (int64_t)table[tok / BS] * kBytes;
+            src.off = tok % BS;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kEntries; ++e)
+                src.blk.p[e] = cache + (int64_t)table[min(st * kEntries + e, last)] * kBytes;
+            src.off = 0;
+        }
+        return src;
+    }
+
+};
+
+// Request a step into ring slot `slot` (wave g of G; see Gather): blk_of and
+// off are the fields of the step's Gather<BS>::Src (passed by value, so the
+// pointers stay in registers).
+template <int G, int BS>
+__device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_per_step(BS)> blk_of,
+                                             int off, bool tiled, int g, int lane)
+{
+    constexpr int kEntries = entries_per_step(BS);
+    constexpr int KC = kChunks - 1;
+    constexpr int J = (KC + G - 1) / G;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = g + G * j;
+        if (G * J == KC || c < KC) {
+            const int q = lane ^ (8 * (c & 1));
+            const int e = BS >= kStep ? 0 : (8 * c) / BS;  // wave-uniform
+            const uint8_t *blk = blk_of.p[0];
+#pragma unroll
+            for (int i = 1; i < kEntries; ++i)  // selects, not a dynamic index
+                if (e == i)
+                    blk = blk_of.p[i];
+            const int row = (BS >= kStep ? off + 8 * c : (8 * c) % BS) + (q & 7);
+            const int u = q >> 3;
+            const int src = tiled ? (row >> 4) * (16 * kDim) + u * 256 + (row & 15) * 16
+                                  : row * kDim + u * 16;
+            __builtin_amdgcn_global_load_lds(blk + src, slot + 1024 * c, 16, 0, kStreamHint);
+        }
+    }
+    if (G == 1 || g == G - 1) {
+        const uint8_t *blk = blk_of.p[0];
+        int row = off + lane;
+        if (BS < kStep) {
+#pragma unroll
+            for (int e = 1; e < kEntries; ++e)
+                if (lane >= e * BS)
+                    blk = blk_of.p[e];
+            row = lane % BS;
+        }
+        __builtin_amdgcn_global_load_lds(blk + BS * kDim + row * 4, slot + kBlock * kDim, 4, 0,
+                                         kStreamHint);
+    }
+}
+
+// Per-token blocks (BS = 1, the plain co-packed layout): token p's 128 K
+// bytes and 4 scale bytes sit at 132 * table[p], so rows are only 4-byte
+// aligned and every token has its own table entry.  A step's 64 entries are
+// staged in LDS (one global->LDS dword load, by wave 0, well ahead: see the
+// kernel), each wave reads the entries its loads need, and K moves with
+// 4-byte global->LDS loads: dword load jj of chunk c writes LDS bytes
+// 1024 c + 256 jj + 4 i from lane i, i.e. byte 4 (i % 4) of granule
+// position 16 jj + i / 4, which holds granule q = position ^ 8 (c & 1): token
+// 8c + (i / 4) % 8, 16-byte granule 2 jj + ((i / 32) ^ (c & 1)).  So each lane
+// needs one entry per chunk, and four loads move a chunk.
+constexpr int kTokLoadsPerChunk = 4;
+
+__device__ __forceinline__ int32_t lds_read_i32(uint32_t addr)
+{
+    int32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, const uint8_t *cache,
+                                               int g, int lane)
+{
+    constexpr int KC = kChunks - 1;
+    constexpr int J = (KC + G - 1) / G;
+    const bool scales = G == 1 || g == G - 1;
+    int32_t ent[J];
+    int32_t ent_s = 0;
+    // Inline asm reads, completed by an explicit wait: the compiler would
+    // otherwise make them wait for every outstanding global->LDS load.
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = g + G * j;
+        ent[j] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * (8 * c + ((lane >> 2) & 7))) : 0;
+    }
+    if (scales)
+        ent_s = lds_read_i32(entries + 4 * lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        asm volatile("" : "+v"(ent[j]));
+        const int c = g + G * j;
+        if (G * J == KC || c < KC) {
+            const uint8_t *src = cache + (int64_t)ent[j] * (kDim + 4) +
+                                 16 * (((lane >> 5) ^ (c & 1))) + 4 * (lane & 3);
+#pragma unroll
+            for (int jj = 0; jj < kTokLoadsPerChunk; ++jj)
+                __builtin_amdgcn_global_load_lds(src + 32 * jj, slot + 1024 * c + 256 * jj, 4, 0,
+                                                 kStreamHint);
+        }
+    }
+    if (scales) {
+        asm volatile("" : "+v"(ent_s));
+        __builtin_amdgcn_global_load_lds(cache + (int64_t)ent_s * (kDim + 4) + kDim,
+                                         slot + kBlock * kDim, 4, 0, kStreamHint);
+    }
+}
+
+// The fewest global->LDS loads any wave of G issues per step, with
+// loads_per_chunk loads per K chunk and the scale load on the last wave.
+constexpr int min_loads_per_step(int G, int loads_per_chunk)
+{
+    int m = 1 << 30;
+    for (int g = 0; g < G; ++g) {
+        int n = g == G - 1 ? 1 : 0;
+        for (int c = g; c < kChunks - 1; c += G)
+            n += loads_per_chunk;
+        m = n < m ? n : m;
+    }
+    return m;
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+
+// Read a ring slot into registers.  Lane (t, g') needs token 32 h + t,
+// granules u = 2j + g', j = 0..3: chunk c = 4h + t/8 (same parity for both
+// tiles), logical granule q = 16 j + 8 g' + t % 8, stored at position
+// q ^ 8 (c & 1) = 16 j + 8 (g' ^ (c & 1)) + t % 8, so read j sits 256 bytes
+// after read 0.  The reads are inline asm because the compiler would
+// otherwise make every LDS read wait for all outstanding global->LDS loads;
+// read_wait() completes them.
+__device__ __forceinline__ void read_block(KStep &k, uint32_t slot, int lane)
+{
+    const int t = lane & 31, gq = lane >> 5;
+    const int c = t >> 3;  // chunk within the tile; tile 1 adds 4 (same parity)
+    const int p0 = 8 * (gq ^ (c & 1)) + (t & 7);
+    const uint32_t a0 = slot + (c * 1024 + p0 * 16);
+    const uint32_t a1 = a0 + 4096;
+    const uint32_t sa = slot + kBlock * kDim + t * 4;
+    asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[0].c[0]) : "v"(a0));
+    asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(k.t[0].c[1]) : "v"(a0));
+    asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[0].c[2]) : "v"(a0));
+    asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(k.t[0].c[3]) : "v"(a0));
+    asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[1].c[0]) : "v"(a1));
+    asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(k.t[1].c[1]) : "v"(a1));
+    asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[1].c[2]) : "v"(a1));
+    asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(k.t[1].c[3]) : "v"(a1));
+    asm volatile("ds_read_b32 %0, %1 offset:0" : "=v"(k.sc[0]) : "v"(sa));
+    asm volatile("ds_read_b32 %0, %1 offset:128" : "=v"(k.sc[1]) : "v"(sa));
+}
+
+// Wait for read_block's results; the registers pass through the asm, so no
+// use of them can be scheduled before the wait.
+__device__ __forceinline__ void read_wait(KStep &k)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(k.t[0].c[0]), "+v"(k.t[0].c[1]), "+v"(k.t[0].c[2]), "+v"(k.t[0].c[3]),
+                   "+v"(k.t[1].c[0]), "+v"(k.t[1].c[1]), "+v"(k.t[1].c[2]), "+v"(k.t[1].c[3]),
+                   "+v"(k.sc[0]), "+v"(k.sc[1])
+                 :
+                 : "memory");
+}
+
+template <int R, int G, int D, int BS, int HT, int MODE = kLogits>
+__global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restrict__ qbuf,
+                                                        const uint8_t *__restrict__ cache,
+                                                        const float *__restrict__ wbuf,
+                                                        const int32_t *__restrict__ ctx_lens,
+                                                        const int32_t *__restrict__ tables,
+                                                        float *__restrict__ logits, DecodeArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t ring_mem[];
+    constexpr int NP = (R + 1) / 2;
+    const int lane = lane_id();
+    const int g = G == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // row group
+    const int s = blockIdx.x % a.split;
+    const int b = blockIdx.x / a.split;
+
+    const int ctx = ctx_lens[b];
+    const int mml = a.mml;
+    const int row0 = g * R;
+    const int nrows = min(R, a.next_n - row0);
+    // Inclusive bound of this wave's first row; row row0 + i covers p <= first_bound + i.
+    const int first_bound = ctx - a.next_n + row0;
+    // Every wave of the workgroup walks the sequence's whole window (the last
+    // row's bound is ctx - 1), so all of them execute the same barriers.
+    const int nvalid = max(min(ctx, mml), 0);
+    const int nsteps = (nvalid + kStep - 1) / kStep;
+    int st0, st1;
+    if constexpr (MODE == kSample) {
+        // chunk s of kSampleChunks (a.split): kSampleSteps steps, evenly spaced
+        const int span = max(nsteps - kSampleSteps, 0);
+        st0 = (int)((int64_t)span * s / (kSampleChunks - 1));
+        st1 = min(st0 + kSampleSteps, nsteps);
+    } else {
+        st0 = (int)((int64_t)nsteps * s / a.split);
+        st1 = (int)((int64_t)nsteps * (s + 1) / a.split);
+    }
+    const int64_t row_base = (int64_t)b * a.next_n + row0;
+    float *out = logits + row_base * mml;
+    const int t = lane & 31;
+    const int half = lane >> 5;
+    const float ninf = -__builtin_inff();
+
+    if (st0 < st1) {
+        constexpr int H = kHeads * HT;
+        Frag q[R][HT];
+        Weights16 w[R][HT];
+        // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f)
+        // and the entries kept so far for it (each row belongs to one wave, and
+        // within it to one half of the lanes, so the count needs no atomics)
+        float fthr[NP];
+        int kept[NP];
+        if constexpr (MODE == kFilter) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const uint32_t tk = a.threshold[row_base + min(2 * i + half, nrows - 1)];
+                fthr[i] = tk == 0u ? __builtin_inff() : key_float(tk);
+                kept[i] = 0;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            // a short last group computes its missing rows as copies of its
+            // last row and never stores them, so the loop body stays branch-free
+            const int64_t row = row_base + min(r, nrows - 1);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                load_frag(q[r][ht], qbuf + row * (H * kDim) + (ht * kHeads + t) * kDim, lane);
+                load_weights(w[r][ht], wbuf + row * H + ht * kHeads, lane);
+            }
+        }
+        // This lane's output row (and column t) within each pair, its window
+        // bound, and whether the row exists.
+        float *orow[NP];
+        int obound[NP];
+        bool ostore[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int rr = 2 * i + half;
+            orow[i] = out + (int64_t)min(rr, nrows - 1) * mml + t;
+            obound[i] = first_bound + rr;
+            ostore[i] = rr < nrows;
+        }
+        const bool clean = a.clean != 0;
+        auto store_step = [&](int step, const float (&tot)[2][NP]) {
+            const int p0 = step * kStep;
+            if constexpr (MODE == kSample) {
+                // columns of chunk s: [s kSampleSteps 64, (s + 1) kSampleSteps 64)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int p = p0 + h * kTile + t;
+                    const int c = s * kSampleSteps * kStep + (p - st0 * kStep);
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        const bool valid = p <= obound[i] && p < mml;
+                        if (ostore[i])
+                            a.sample[(row_base + 2 * i + half) * kSampleCols + c] =
+                                valid ? tot[h][i] : ninf;
+                    }
+                }
+                return;
+            }
+            if constexpr (MODE == kFilter) {
+                const uint32_t lt = (1u << t) - 1u;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int p = p0 + h * kTile + t;
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        const bool keep =
+                            ostore[i] && p <= obound[i] && p < mml && tot[h][i] >= fthr[i];
+                        const uint64_t bal = __ballot(keep);
+                        // lanes 0..31 hold row 2i, lanes 32..63 row 2i + 1
+                        const uint32_t mine = half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+                        if (keep)
+                            a.entries[(row_base + 2 * i + half) * a.ent_stride + st0 * kStep +
+                                      kept[i] + __popc(mine & lt)] = fused_entry(tot[h][i], p);
+                        kept[i] += __popc(mine);
+                    }
+                }
+                return;
+            }
+            if (p0 + kStep - 1 <= first_bound && p0 + kStep <= mml) {
+                // every column of the step is inside every row's window
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < NP; ++i)
+                        if (ostore[i])
+                            orow[i][p0 + h * kTile] = tot[h][i];
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int p = p0 + h * kTile + t;
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        const bool valid = p <= obound[i];
+                        if (ostore[i] && p < mml && (valid || clean))
+                            orow[i][p0 + h * kTile] = valid ? tot[h][i] : ninf;
+                    }
+                }
+            }
+        };
+
+        const int32_t *table = tables + (int64_t)b * a.mbps;
+        const bool tiled = a.tiled != 0;
+        lds_u8 *ring = (lds_u8 *)ring_mem;
+        const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+        using Gth = Gather<(BS == 1 ? kBlock : BS)>;  // unused for BS = 1
+        const int last_entry = (nvalid - 1) / BS;
+        // BS = 1: table ring of 2D - 2 steps of 64 entries after the K ring.
+        // Entries for step y are loaded (by wave 0) in the iteration that
+        // requests K for step y - D + 1, before that request, and read in the
+        // iteration that requests step y: by then the wait for step
+        // y - D + 1 has covered them, and the barrier published them.
+        constexpr int kTabSlots = 2 * D - 2;
+        lds_u8 *tring = ring + D * kSlotBytes;
+        const uint32_t tring_addr = ring_addr + D * kSlotBytes;
+        auto request_table = [&](int y) {  // wave 0 only
+            const int tok = min(y * kStep + lane, last_entry);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(table + tok),
+                                             tring + ((y - st0) % kTabSlots) * (kStep * 4), 4, 0, 0);
+        };
+        // Fill D-1 slots (fewer when the split has fewer steps).
+        if constexpr (BS == 1) {
+            if (g == 0) {
+#pragma unroll
+                for (int i = 0; i < kTabSlots; ++i)
+                    if (st0 + i < st1)
+                        request_table(st0 + i);
+            }
+            wait_vm<0>();
+            __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int i = 0; i < D - 1; ++i)
+                if (st0 + i < st1)
+                    request_tokens<G>(ring + i * kSlotBytes, tring_addr + i * (kStep * 4), cache, g,
+                                      lane);
+        } else {
+#pragma unroll
+            for (int i = 0; i < D - 1; ++i)
+                if (st0 + i < st1) {
+                    const typename Gth::Src src = Gth::fetch(cache, table, st0 + i, last_entry);
+                    request_step<G, BS>(ring + i * kSlotBytes, src.blk, src.off, tiled, g, lane);
+                }
+        }
+        // Between requesting block k and waiting for it a wave requests the
+        // D - 2 following blocks, at least min_loads_per_step loads each, so
+        // waiting until at most that many loads are outstanding guarantees
+        // block k (loads complete in order; stores and table loads counted as
+        // well only make the wait stricter).  In the last D - 2 steps fewer
+        // blocks follow and the wave waits for everything.
+        // (vmcnt holds at most 63; a smaller count is a stricter wait)
+        constexpr int kWaitRaw = (D - 2) * min_loads_per_step(G, BS == 1 ? kTokLoadsPerChunk : 1);
+        constexpr int kWait = kWaitRaw < 63 ? kWaitRaw : 63;
+        int rd = 0;      // slot of step st
+        int wr = D - 1;  // slot of step st + D - 1
+        // Block-table entries are read one step ahead: a scalar load is only
+        // waited for together with every outstanding LDS read, so its result
+        // must not be needed between read_block and read_wait.
+        typename Gth::Src next{};
+        if constexpr (BS != 1)
+            next = Gth::fetch(cache, table, min(st0 + D - 1, st1 - 1), last_entry);
+        float prev_tot[2][NP];
+        for (int st = st0; st < st1; ++st) {
+            // this wave's part of block st has landed ...
+            if (st + D - 2 < st1)
+                wait_vm<kWait>();
+            else
+                wait_vm<0>();
+            // ... and every wave's part; nobody reads slot st-1 any more
+            __builtin_amdgcn_s_barrier();
+            if constexpr (BS == 1) {
+                if (g == 0 && st + kTabSlots < st1)
+                    request_table(st + kTabSlots);
+                if (st + D - 1 < st1)
+                    request_tokens<G>(ring + wr * kSlotBytes,
+                                      tring_addr + ((st + D - 1 - st0) % kTabSlots) * (kStep * 4),
+                                      cache, g, lane);
+            } else {
+                if (st + D - 1 < st1)
+                    request_step<G, BS>(ring + wr * kSlotBytes, next.blk, next.off, tiled, g,
+                                        lane);
+                next = Gth::fetch(cache, table, min(st + D, st1 - 1), last_entry);
+            }
+            KStep kb;
+            read_block(kb, ring_addr + rd * kSlotBytes, lane);
+            if (st > st0)
+                store_step(st - 1, prev_tot);
+            rd = (rd + 1 == D) ? 0 : rd + 1;
+            wr = (wr + 1 == D) ? 0 : wr + 1;
+            read_wait(kb);
+            step_scores<R, HT>(kb, q, w, prev_tot);
+        }
+        store_step(st1 - 1, prev_tot);
+        if constexpr (MODE == kFilter) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                if (ostore[i] && t == 0)
+                    a.counts[(row_base + 2 * i + half) * a.split + s] = kept[i];
+        }
+        // No global->LDS load may still be in flight once the workgroup ends
+        // and its LDS goes to the next workgroup.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if constexpr (MODE == kSample) {
+        // the chunk's columns past its last step (short sequences) are -inf
+        const int done = max(st1 - st0, 0) * kStep;
+        for (int r = 0; r < nrows; ++r)
+            for (int c = done + lane; c < kSampleSteps * kStep; c += 64)
+                a.sample[(row_base + r) * kSampleCols + s * kSampleSteps * kStep + c] = ninf;
+        return;
+    }
+    if constexpr (MODE == kFilter) {
+        // a workgroup with no step (empty sequence) keeps nothing
+        if (st0 >= st1 && lane == 0)
+            for (int r = 0; r < nrows; ++r)
+                a.counts[(row_base + r) * a.split + s] = 0;
+        return;
+    }
+    if (a.clean) {
+        const int64_t f0 = min((int64_t)nsteps * kStep, (int64_t)mml);
+        for (int r = 0; r < nrows; ++r)
+            fill_neg_inf(out + (int64_t)r * mml, f0, mml, s, a.split, lane);
+    }
+}
+
+template <int R, int G, int D, int BS, int HT = 1, int MODE = kLogits>
+hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
+{
+    const size_t lds = (size_t)ring_lds_bytes<D, BS>();
+    hipLaunchKernelGGL((decode_kernel<R, G, D, BS, HT, MODE>), dim3(grid), dim3(64 * G), lds, stream,
+                       p.q, p.cache, p.weights, p.context_lens, p.block_tables, p.logits, a);
+    return hipGetLastError();
+}
+
+// Kernel arguments of a validated launch.
+inline DecodeArgs decode_args(const DecodeLaunch &p)
+{
+    DecodeArgs a;
+    a.mml = (int)p.max_model_len;
+    a.next_n = p.next_n;
+    a.mbps = p.max_blocks_per_seq;
+    a.clean = p.clean;
+    a.groups = (p.next_n + p.rows - 1) / p.rows;
+    a.split = p.split_kv;
+    a.tiled = p.tiled;
+    a.sample = p.sample;
+    a.threshold = p.threshold;
+    a.entries = p.entries;
+    a.counts = p.counts;
+    a.ent_stride = p.ent_stride;
+    return a;
+}
+
+} // namespace
+} // namespace mqa

@@ -46,7 +46,8 @@ struct DecodeLaunch {
     int head_tiles;  // num_heads / 32: 1, 2 or 4 (2 and 4: block size 64, depth 4)
     int tiled;       // 1: K rows in the preshuffled (16,16) order (block size >= 16)
     // fused top-k only (zero / NULL for the logits call):
-    int mode;              // 0 logits, 1 sample, 2 filter (modes 1, 2: 32 heads, block 64, depth 3)
+    int mode;              // 0 logits, 1 sample, 2 filter (modes 1, 2: the default depth,
+                           // 3 for 64-token blocks at 32 heads, else 4)
     float *sample;         // [rows][kFusedSampleCols]
     const uint32_t *threshold;  // [rows]
     uint64_t *entries;     // [rows][ent_stride]
@@ -116,13 +117,15 @@ struct FusedTopkLaunch {
     int mml;
     int k;
     int split;  // the filtering decode's KV split
-    // what a row needs to be recomputed in full (64-token blocks, 32 heads)
+    // what a row needs to be recomputed in full
     const uint8_t *q;
     const uint8_t *cache;
     const float *weights;
     const int32_t *block_tables;
     int max_blocks_per_seq;
     int tiled;
+    int block_size;  // 1, 16, 64 or 128
+    int head_tiles;  // num_heads / 32: 1, 2 or 4
 };
 
 struct KcacheLaunch {
@@ -141,6 +144,7 @@ int decode_ring_bytes(int depth);
 
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
+hipError_t launch_decode_fused(const DecodeLaunch &p, hipStream_t stream);  // modes 1 and 2
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream);
 hipError_t launch_fused_threshold(const FusedTopkLaunch &p, hipStream_t stream);
 hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream);

@@ -861,6 +861,7 @@ struct FusedRowArgs {
     const int32_t *tables;
     int mbps;
     int tiled;
+    int block_size;  // tokens per cache block: 1, 16, 64 or 128
 };
 
 struct ThresholdShared {
@@ -914,46 +915,90 @@ __global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
 
 // Row r's logits (the decode call's values, -inf outside the window) into
 // x[0, mml): the workgroup's waves take the row's 64-token steps in turn and
-// compute them with the decode kernel's contraction and epilogue (one row per
-// wave, K straight from the cache), so every value equals the decode call's.
+// compute them with the decode kernel's contraction and epilogue (one row of
+// 32 HT heads per wave, K straight from the cache), so every value equals the
+// decode call's.  Each lane finds its token's block through the table, for
+// any block size; entries past the last one holding a window token are never
+// read (a later token reuses it, and its value is never kept).
+template <int HT>
 __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, int r, int tid,
                                               int lane, int wave)
 {
+    constexpr int H = kHeads * HT;
     const int b = r / ra.next_n, j = r % ra.next_n;
     const int ctx = ra.ctx_lens[b];
     const int nvalid = max(min(ctx, ra.mml), 0);
     const int nsteps = (nvalid + kStep - 1) / kStep;
     const int bound = ctx - ra.next_n + j;  // inclusive
     const int t = lane & 31, g = lane >> 5;
-    Frag q[1][1];
-    Weights16 w[1][1];
-    load_frag(q[0][0], ra.q + (int64_t)r * (kHeads * kDim) + t * kDim, lane);
-    load_weights(w[0][0], ra.weights + (int64_t)r * kHeads, lane);
+    const int bs = ra.block_size;
+    const int64_t blk_bytes = (int64_t)bs * (kDim + 4);
+    const int last = max(nvalid - 1, 0) / bs;
+    // With 16 waves a workgroup has 128 VGPRs per lane, so at most one head
+    // tile's Q and weights stay in registers: 32 heads keep theirs for the
+    // whole row, more heads reload them per step, tile by tile, summed in the
+    // decode kernel's order.
+    const uint8_t *qrow = ra.q + (int64_t)r * (H * kDim) + t * kDim;
+    const float *wrow = ra.weights + (int64_t)r * H;
+    Frag q0;
+    Weights16 w0;
+    if constexpr (HT == 1) {
+        load_frag(q0, qrow, lane);
+        load_weights(w0, wrow, lane);
+    }
     const int32_t *table = ra.tables + (int64_t)b * ra.mbps;
     const float ninf = -__builtin_inff();
     for (int st = wave; st < nsteps; st += kWaves) {
-        const uint8_t *blk = ra.cache + (int64_t)table[st] * kBlockBytes;
         KStep k;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int slot = kTile * h + t;
+            const int p = st * kStep + kTile * h + t;
+            const int slot = p % bs;
+            const uint8_t *blk = ra.cache + (int64_t)table[min(p / bs, last)] * blk_bytes;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int u = 2 * c + g;  // 16-byte granule of the row
                 const int off = ra.tiled ? (slot >> 4) * (16 * kDim) + u * 256 + (slot & 15) * 16
                                          : slot * kDim + u * 16;
-                k.t[h].c[c] = *reinterpret_cast<const i32x4 *>(blk + off);
+                if (bs == 1) {
+                    // per-token records are 132 bytes: K rows only 4-byte aligned
+                    const int *src = reinterpret_cast<const int *>(blk + off);
+                    k.t[h].c[c] = i32x4{src[0], src[1], src[2], src[3]};
+                } else {
+                    k.t[h].c[c] = *reinterpret_cast<const i32x4 *>(blk + off);
+                }
             }
-            k.sc[h] = *reinterpret_cast<const float *>(blk + kBlock * kDim + 4 * slot);
+            k.sc[h] = *reinterpret_cast<const float *>(blk + bs * kDim + 4 * slot);
         }
-        float tot[2][1];
-        step_scores<1, 1>(k, q, w, tot);
+        float part[2];
+        if constexpr (HT == 1) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                part[h] = relu_weight_sum(row_scores(q0, k.t[h]), w0);
+        } else {
+#pragma unroll 1
+            for (int ht = 0; ht < HT; ++ht) {
+                Frag q;
+                Weights16 w;
+                load_frag(q, qrow + ht * (kHeads * kDim), lane);
+                load_weights(w, wrow + ht * kHeads, lane);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float v = relu_weight_sum(row_scores(q, k.t[h]), w);
+                    part[h] = ht == 0 ? v : part[h] + v;
+                }
+            }
+        }
+        float tot[2];  // the cross-lane step runs with every lane active
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            tot[h] = pair_head_sum(part[h], part[h]) * k.sc[h];
         if (lane < 32) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int p = st * kStep + h * kTile + t;
                 if (p < ra.mml)
-                    x[p] = p <= bound ? tot[h][0] : ninf;
+                    x[p] = p <= bound ? tot[h] : ninf;
             }
         }
     }
@@ -961,6 +1006,7 @@ __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, 
         x[p] = ninf;
 }
 
+template <int HT>
 __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
                                                                 const int *__restrict__ counts,
                                                                 int split, int k,
@@ -1014,13 +1060,28 @@ __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
     } else {
         // the row's own segment region (>= mml floats) now holds its logits
         float *x = reinterpret_cast<float *>(row);
-        recompute_row(x, ra, r, tid, lane, wave);
+        recompute_row<HT>(x, ra, r, tid, lane, wave);
         __threadfence_block();
         __syncthreads();
         n = radix_select(sh, x, ra.mml, k, tid, lane, wave);
     }
     __syncthreads();
     sort_and_write(sh, n, out, k, tid, lane, wave);
+}
+
+template <int HT>
+hipError_t launch_fused_select_ht(const FusedTopkLaunch &p, const FusedRowArgs &ra,
+                                  hipStream_t stream)
+{
+    static std::atomic<uint64_t> raised{0};
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&fused_select_kernel<HT>),
+                                   (int)sizeof(TopkShared), raised);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fused_select_kernel<HT>, dim3(p.batch * p.next_n), dim3(kThreads),
+                       sizeof(TopkShared), stream, ra, p.ws->counts, p.split, p.k, p.indices,
+                       p.ws->recomputed);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -1034,11 +1095,6 @@ hipError_t launch_fused_threshold(const FusedTopkLaunch &p, hipStream_t stream)
 
 hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream)
 {
-    static std::atomic<uint64_t> raised{0};
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&fused_select_kernel),
-                                   (int)sizeof(TopkShared), raised);
-    if (e != hipSuccess)
-        return e;
     FusedRowArgs ra;
     ra.entries = p.ws->entries;
     ra.ent_stride = p.ws->ent_stride;
@@ -1051,10 +1107,13 @@ hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream)
     ra.tables = p.block_tables;
     ra.mbps = p.max_blocks_per_seq;
     ra.tiled = p.tiled;
-    hipLaunchKernelGGL(fused_select_kernel, dim3(p.batch * p.next_n), dim3(kThreads),
-                       sizeof(TopkShared), stream, ra, p.ws->counts, p.split, p.k, p.indices,
-                       p.ws->recomputed);
-    return hipGetLastError();
+    ra.block_size = p.block_size;
+    switch (p.head_tiles) {
+    case 1: return launch_fused_select_ht<1>(p, ra, stream);
+    case 2: return launch_fused_select_ht<2>(p, ra, stream);
+    case 4: return launch_fused_select_ht<4>(p, ra, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream)

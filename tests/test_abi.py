@@ -179,12 +179,23 @@ def test_fused_topk_validation(lib):
     assert _fused(lib, nulls, k=0) == E.MQA_ERR_INVALID_ARG
     assert "k must be" in mqa.last_error()
     assert _fused(lib, nulls, k=2049) == E.MQA_ERR_INVALID_ARG
-    assert _fused(lib, nulls, H=64) == E.MQA_ERR_UNSUPPORTED
-    assert _fused(lib, nulls, bs=16) == E.MQA_ERR_UNSUPPORTED
-    assert _fused(lib, nulls, bs=1) == E.MQA_ERR_UNSUPPORTED
+    # the shapes the decode takes, checked before any pointer
+    assert _fused(lib, nulls, H=48) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, H=64, bs=16) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, bs=32) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, D=64) == E.MQA_ERR_UNSUPPORTED
-    bad = E.Tunables(ring_depth=4)
-    assert _fused(lib, nulls, tun=ctypes.byref(bad)) == E.MQA_ERR_INVALID_ARG
+    for H, bs in ((64, 64), (128, 64), (32, 16), (32, 1), (32, 128)):
+        assert _fused(lib, nulls, H=H, bs=bs) == E.MQA_ERR_INVALID_ARG
+        assert "NULL" in mqa.last_error()
+    # the ring depth is the logits call's default: 3 for 64-token blocks at 32 heads, else 4
+    assert _fused(lib, nulls, tun=ctypes.byref(E.Tunables(ring_depth=4))) == E.MQA_ERR_INVALID_ARG
+    assert "ring depth" in mqa.last_error()
+    assert _fused(lib, nulls, bs=16, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
+        E.MQA_ERR_INVALID_ARG
+    assert "ring depth" in mqa.last_error()
+    assert _fused(lib, nulls, bs=16, tun=ctypes.byref(E.Tunables(ring_depth=4))) == \
+        E.MQA_ERR_INVALID_ARG
+    assert "NULL" in mqa.last_error()
     assert _fused(lib, nulls, B=0) == 0          # nothing to do, nothing dereferenced
     assert _fused(lib, nulls, mml=0) == 0
     assert _fused(lib, nulls) == E.MQA_ERR_INVALID_ARG
