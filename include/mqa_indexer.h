@@ -84,8 +84,8 @@ typedef struct mqa_tunables {
  * sweeps) with head_dim 128, and for prefill also head_dim 64 (the head dims
  * of the aiter PR 5046 page's test sweep, "Test Plan").  kv_block_size: 0 asks
  * about prefill; 1, 16, 64 or 128 about paged decode with blocks of that many
- * tokens (64 only with 64 or 128 heads).  Returns 1 if the current HIP device
- * is gfx950 and the shape is supported, else 0.  Never fails.
+ * tokens (at every head count).  Returns 1 if the current HIP device is gfx950
+ * and the shape is supported, else 0.  Never fails.
  */
 int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
 
@@ -164,8 +164,8 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * Entries past that are never read.  Scales must be >= 0.  Cache slots past a
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
- * kv_block_size 1, 16, 64 or 128 (ring_depth tunable other than 4 only with
- * 64 and 32 heads).  kv_layout MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED (the
+ * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads (ring_depth tunable
+ * other than 4 only with kv_block_size 64 and 32 heads).  kv_layout MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED (the
  * latter not with kv_block_size 1).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
  * a bad kv_layout, negative sizes, NULL or misaligned pointers ->

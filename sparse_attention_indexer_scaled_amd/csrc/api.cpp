@@ -82,15 +82,13 @@ int check_device()
 // 32, 64 or 128 index heads (the pages sweep all three); head dim 128, or 64
 // for prefill (the prefill page's test sweep covers head dims 64 and 128, the
 // decode page's only 128); cache blocks of 1, 16, 64 or 128 tokens for decode
-// (0 asks about prefill), 64 only with more than 32 heads.
+// (0 asks about prefill), at every head count.
 bool shape_supported(int num_heads, int head_dim, int kv_block_size)
 {
     if (num_heads != 32 && num_heads != 64 && num_heads != 128)
         return false;
     if (head_dim != 128 && !(head_dim == 64 && kv_block_size == 0))
         return false;
-    if (num_heads != 32)
-        return kv_block_size == 0 || kv_block_size == 64;
     return kv_block_size == 0 || kv_block_size == 1 || kv_block_size == 16 ||
            kv_block_size == 64 || kv_block_size == 128;
 }
@@ -229,8 +227,8 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
                     "(got %d)", kv_layout);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "decode supports num_heads=32 with kv_block_size 1, 16, 64 or 128, or "
-                    "num_heads 64 / 128 with kv_block_size 64; head_dim=128 (got %d, %d, %d)",
+                    "decode supports num_heads 32, 64 or 128, head_dim 128 and kv_block_size 1, "
+                    "16, 64 or 128 (got %d, %d, %d)",
                     num_heads, head_dim, kv_block_size);
     if (kv_layout == MQA_KV_PRESHUFFLED && kv_block_size < 16)
         return fail(MQA_ERR_UNSUPPORTED, "the preshuffled layout needs kv_block_size 16, 64 or 128 "
@@ -358,9 +356,9 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
         return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "the fused top-k takes the decode's shapes: num_heads=32 with kv_block_size 1, "
-                    "16, 64 or 128, or num_heads 64 / 128 with kv_block_size 64; head_dim=128 "
-                    "(got %d, %d, %d)", num_heads, head_dim, kv_block_size);
+                    "the fused top-k takes the decode's shapes: num_heads 32, 64 or 128, "
+                    "head_dim 128, kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)", num_heads,
+                    head_dim, kv_block_size);
     // the sample and filter modes are built for the logits call's default ring
     const int depth = (kv_block_size == 64 && num_heads == 32) ? 3 : 4;
     if (tun && tun->ring_depth != 0 && tun->ring_depth != depth)

@@ -598,6 +598,77 @@ hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hip
     return hipGetLastError();
 }
 
+// The kernels a (rows per wave R, waves G, head tiles HT, mode) launch can
+// take, by block size and ring depth: 64-token blocks at 32 heads take ring
+// depths 2..7 for the logits call and 3 for the fused top-k's modes; every
+// other layout takes depth 4.  (Q and weights of a wave's rows stay in VGPRs,
+// so R HT <= 4.)
+template <int R, int G, int HT, int MODE>
+hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
+{
+    if constexpr (R * HT > 4) {
+        return hipErrorInvalidValue;
+    } else {
+        if constexpr (HT == 1) {
+            if (p.block_size == 64) {
+                if constexpr (MODE == kLogits) {
+                    switch (p.depth) {
+                    case 2: return launch_rgdb<R, G, 2, 64, 1, MODE>(p, a, grid, stream);
+                    case 3: return launch_rgdb<R, G, 3, 64, 1, MODE>(p, a, grid, stream);
+                    case 4: return launch_rgdb<R, G, 4, 64, 1, MODE>(p, a, grid, stream);
+                    case 5: return launch_rgdb<R, G, 5, 64, 1, MODE>(p, a, grid, stream);
+                    case 6: return launch_rgdb<R, G, 6, 64, 1, MODE>(p, a, grid, stream);
+                    case 7: return launch_rgdb<R, G, 7, 64, 1, MODE>(p, a, grid, stream);
+                    default: return hipErrorInvalidValue;
+                    }
+                } else {
+                    return p.depth == 3 ? launch_rgdb<R, G, 3, 64, 1, MODE>(p, a, grid, stream)
+                                        : hipErrorInvalidValue;
+                }
+            }
+        }
+        if (p.depth != 4)
+            return hipErrorInvalidValue;
+        switch (p.block_size) {
+        case 1: return launch_rgdb<R, G, 4, 1, HT, MODE>(p, a, grid, stream);
+        case 16: return launch_rgdb<R, G, 4, 16, HT, MODE>(p, a, grid, stream);
+        case 64:
+            if constexpr (HT > 1)
+                return launch_rgdb<R, G, 4, 64, HT, MODE>(p, a, grid, stream);
+            else
+                return hipErrorInvalidValue;  // handled above
+        case 128: return launch_rgdb<R, G, 4, 128, HT, MODE>(p, a, grid, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+}
+
+// (rows, row groups) pairs that next_n in 1..8 can produce
+template <int HT, int MODE>
+hipError_t launch_ht(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
+{
+    switch (p.rows * 16 + a.groups) {
+    case 1 * 16 + 1: return launch_rg<1, 1, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 2: return launch_rg<1, 2, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 3: return launch_rg<1, 3, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 4: return launch_rg<1, 4, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 5: return launch_rg<1, 5, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 6: return launch_rg<1, 6, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 7: return launch_rg<1, 7, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 8: return launch_rg<1, 8, HT, MODE>(p, a, grid, stream);
+    case 2 * 16 + 1: return launch_rg<2, 1, HT, MODE>(p, a, grid, stream);
+    case 2 * 16 + 2: return launch_rg<2, 2, HT, MODE>(p, a, grid, stream);
+    case 2 * 16 + 3: return launch_rg<2, 3, HT, MODE>(p, a, grid, stream);
+    case 2 * 16 + 4: return launch_rg<2, 4, HT, MODE>(p, a, grid, stream);
+    case 3 * 16 + 1: return launch_rg<3, 1, HT, MODE>(p, a, grid, stream);
+    case 3 * 16 + 2: return launch_rg<3, 2, HT, MODE>(p, a, grid, stream);
+    case 3 * 16 + 3: return launch_rg<3, 3, HT, MODE>(p, a, grid, stream);
+    case 4 * 16 + 1: return launch_rg<4, 1, HT, MODE>(p, a, grid, stream);
+    case 4 * 16 + 2: return launch_rg<4, 2, HT, MODE>(p, a, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 // Kernel arguments of a validated launch.
 inline DecodeArgs decode_args(const DecodeLaunch &p)
 {

@@ -331,6 +331,14 @@ CONFIGS = {
              ctx=131072, mml=131072, preshuffle=True),
     # the long prefill chunk at head dim 64
     15: dict(kind="prefill", name="prefill_M4096_N32768_d64", M=4096, N=32768, D=64),
+    # the headline decode shape in 128-token blocks at 32, 64 and 128 heads
+    # (the block size the next_n-tiling issue page quotes its head sweep on)
+    18: dict(kind="decode", name="decode_B16_nn6_ctx131072_bs128", B=16, next_n=6, ctx=131072,
+             mml=131072, block_size=128),
+    19: dict(kind="decode", name="decode_B16_nn6_ctx131072_h64_bs128", B=16, next_n=6,
+             ctx=131072, mml=131072, H=64, block_size=128),
+    20: dict(kind="decode", name="decode_B16_nn6_ctx131072_h128_bs128", B=16, next_n=6,
+             ctx=131072, mml=131072, H=128, block_size=128),
 }
 
 

@@ -122,7 +122,9 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls, bs=0) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, H=48) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, D=64) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert _decode(lib, nulls, H=64, bs=16) == mqa._native.MQA_ERR_UNSUPPORTED
+    for H in (64, 128):
+        for bs in (1, 16, 128):
+            assert _decode(lib, nulls, H=H, bs=bs) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
     bad = _native.Tunables(rows_per_block=2)  # 128 heads: one row per wave
     assert _decode(lib, nulls, H=128, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
     assert _decode(lib, nulls, layout=2) == mqa._native.MQA_ERR_INVALID_ARG
@@ -181,10 +183,9 @@ def test_fused_topk_validation(lib):
     assert _fused(lib, nulls, k=2049) == E.MQA_ERR_INVALID_ARG
     # the shapes the decode takes, checked before any pointer
     assert _fused(lib, nulls, H=48) == E.MQA_ERR_UNSUPPORTED
-    assert _fused(lib, nulls, H=64, bs=16) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, bs=32) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, D=64) == E.MQA_ERR_UNSUPPORTED
-    for H, bs in ((64, 64), (128, 64), (32, 16), (32, 1), (32, 128)):
+    for H, bs in ((64, 64), (128, 64), (32, 16), (32, 1), (32, 128), (64, 16), (128, 1)):
         assert _fused(lib, nulls, H=H, bs=bs) == E.MQA_ERR_INVALID_ARG
         assert "NULL" in mqa.last_error()
     # the ring depth is the logits call's default: 3 for 64-token blocks at 32 heads, else 4

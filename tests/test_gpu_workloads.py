@@ -1,4 +1,4 @@
-"""The five named workloads at full size, in the launch configuration the
+"""The named logits workloads at full size, in the launch configuration the
 benchmark times (all tunables left to the host heuristic, clean_logits on).
 
 Whole-output checks: the -inf mask equals the window predicate exactly at every
@@ -61,7 +61,7 @@ def test_prefill_workload(idx):
     assert_parity(out[rows], ref, mag, f"workload{idx}")
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14])
+@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20])
 def test_decode_workload(idx):
     t0 = time.time()
     d = inputs.make_config(idx, poison=True)
