@@ -26,9 +26,11 @@
 //   - Per 32-token tile and row: two fp8 MFMAs, the in-lane relu.weight sum
 //     over 16 heads, one permlane32 swap + add per row pair, kv_scale once per
 //     column (the hoist: kv_scale >= 0, relu positive-homogeneous).
-//   - A step's results are stored one step later, before that step's next
-//     request, so the stores retire while the next step computes and never
-//     hold up a wait for the ring.
+//   - A step's results are stored one step later, after that step's request
+//     and LDS reads, so the stores retire while the next step computes.
+//     (Stored before the request, they lead the compiler to wait for every
+//     outstanding load before each global->LDS load in some instantiations:
+//     128 heads ran at half speed.)
 // Positions past the sequence's context up to max_model_len are written -inf
 // by the same waves.  A position is selected by an integer compare, never by
 // arithmetic, so cache slots past the context (which may hold NaN bytes)
@@ -535,14 +537,6 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                 wait_vm<0>();
             // ... and every wave's part; nobody reads slot st-1 any more
             __builtin_amdgcn_s_barrier();
-            // The previous step's results go out before the next request: one
-            // counter tracks a wave's loads and stores in issue order, so
-            // stores issued after the request would, at the next step's wait,
-            // force that request to land as well (one block in flight
-            // instead of D - 1).  Issued first, they have a whole step to
-            // complete.
-            if (st > st0)
-                store_step(st - 1, prev_tot);
             if constexpr (BS == 1) {
                 if (g == 0 && st + kTabSlots < st1)
                     request_table(st + kTabSlots);
@@ -558,6 +552,8 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
             }
             KStep kb;
             read_block(kb, ring_addr + rd * kSlotBytes, lane);
+            if (st > st0)
+                store_step(st - 1, prev_tot);
             rd = (rd + 1 == D) ? 0 : rd + 1;
             wr = (wr + 1 == D) ? 0 : wr + 1;
             read_wait(kb);
