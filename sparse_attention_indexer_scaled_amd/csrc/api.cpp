@@ -275,9 +275,12 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     // device-resident context lengths are not visible without a sync).
     // Measured on MI355X:
     //   rows: every wave of a workgroup reads the same LDS ring, so all next_n
-    //         rows share one HBM stream whatever the row split; 2 waves per
-    //         workgroup (e.g. next_n 6 -> 2 x 3 rows) keep each wave within 256
-    //         registers, 2 waves per SIMD.
+    //         rows share one HBM stream whatever the row split.  From next_n 4
+    //         on, 3 or 4 waves of at most 2 rows (at most ~160 VGPRs, 3 waves
+    //         per SIMD) beat 2 waves of 3 or 4 rows: next_n 6 as 3 x 2 rows
+    //         68.5 against 69.7 us, next_n 4 as 4 x 1 row 144.6 against
+    //         146.7 us (ragged batch), each the mean of three alternating runs.
+    //         Below that, ceil(next_n / 2) rows per wave.
     //   depth: 3 steps (25 KiB) per workgroup for 64-token blocks and 32
     //          heads (the other layouts instantiate 4 only); deeper rings cost
     //          workgroups per CU and measured slower.
@@ -285,7 +288,8 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     //          per workgroup at the longest context, but at least 2 steps;
     //          more workgroups per sequence than that measured slower (longer
     //          prologues relative to the work, more concurrent streams).
-    int rows = t.rows_per_block ? t.rows_per_block : (next_n == 1 ? 1 : (next_n + 1) / 2);
+    const int rows_default = next_n == 4 ? 1 : next_n > 4 ? 2 : (next_n + 1) / 2;
+    int rows = t.rows_per_block ? t.rows_per_block : rows_default;
     rows = std::min(std::min(rows, next_n), max_rows);
     p.head_tiles = head_tiles;
     p.rows = rows;
