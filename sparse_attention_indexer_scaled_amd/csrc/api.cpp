@@ -165,13 +165,15 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     p.N = N;
     p.clean = clean_logits ? 1 : 0;
     // Heuristic (measured on MI355X; both pages, "Technical Details", make
-    // the row block, split and wave count host-chosen): for long chunks 8 rows
-    // per wave share each K step (1 wave per SIMD; K is re-read per row block
-    // from L2, so a larger block means less L2 traffic) with one wave per
-    // workgroup; short chunks take 4 rows and 4 waves for parallelism; and
-    // enough column splits for ~2048 workgroups while each wave keeps >= 4
-    // steps.  High-m first for long causal chunks (aiter PR 5046 page,
-    // "Technical Details": N > 2048).
+    // the row block, split and wave count host-chosen): 4 rows per wave share
+    // each K step, with one wave per workgroup for long chunks and 4 waves for
+    // short ones; and enough column splits for ~2048 workgroups while each
+    // wave keeps >= 4 steps.  4 rows (228 VGPRs, 2 waves per SIMD) measured
+    // faster than 8 rows (1 wave per SIMD) on the long chunk although K is
+    // re-read from L2 twice as often: M 4096, N 32768 took 525 against 536 us
+    // at head dim 128 and 356 against 384 us at head dim 64 (means of three
+    // alternating runs on one box).  High-m first for long causal chunks
+    // (aiter PR 5046 page, "Technical Details": N > 2048).
     //   Small problems (at most 16384 row-steps, e.g. 64 rows x 512
     //   columns) are latency-bound: one row and one wave per workgroup and
     //   splits down to 2 steps per wave measured 2.3x faster than 4 rows x 4
@@ -180,7 +182,7 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     p.head_dim = head_dim;
     const int64_t steps = ceil_div(N, 64);
     const bool small = M < 1024 && (int64_t)M * steps <= 16384;
-    p.block_m = t.block_m ? t.block_m : (small ? 1 : std::min(M >= 1024 ? 8 : 4, max_block_m));
+    p.block_m = t.block_m ? t.block_m : (small ? 1 : std::min(4, max_block_m));
     p.num_warps = t.num_warps ? t.num_warps : (M >= 1024 || small ? 1 : 4);
     const int64_t nrb = ceil_div(M, p.block_m);
     if (t.split_n) {
