@@ -115,7 +115,7 @@ class Workload:
                         ctx=dev(host.context_lens), bt=dev(host.block_tables))
             self.out_shape = (host.B * host.next_n, host.max_model_len)
             self.bytes = workload.decode_essential_bytes(host.B, host.next_n, host.context_lens,
-                                                         host.max_model_len, H=host.H,
+                                                         host.max_model_len, H=host.H, D=host.D,
                                                          block_size=host.block_size)
             self.pairs = workload.decode_valid_pairs(host.next_n, host.context_lens,
                                                      host.max_model_len)
@@ -344,7 +344,7 @@ def cpu_baseline(wl, budget_s=12.0):
     dt = time.time() - t0
     ctx = h.context_lens[done]
     nbytes = workload.decode_essential_bytes(len(done), h.next_n, ctx, h.max_model_len, H=h.H,
-                                             block_size=h.block_size)
+                                             D=h.D, block_size=h.block_size)
     return {"value": round(nbytes / dt / 1e12, 8), "unit": "TB/s", "cores": nthreads,
             "kind": "oracle", "cpu": cpu_model(), "seconds": round(dt, 2),
             "sample": "%d of %d sequences (all %d rows each, every position to max_model_len) of %s"
@@ -593,7 +593,7 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20)
+        [i for i in (1, 4, 3, 0, 5, 6, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21)
          if i != args.workload]
     results, head = {}, None
     for idx in order:
@@ -623,11 +623,11 @@ def main():
     elif decode or wl.kind == "fused_topk":
         config = {"workload": wl.cfg["name"], "batch": h.B, "next_n": h.next_n,
                   "context": int(h.context_lens.max()), "max_model_len": h.max_model_len,
-                  "heads": h.H, "head_dim": 128, "kv_block_size": h.block_size, "cold": not args.hot}
+                  "heads": h.H, "head_dim": h.D, "kv_block_size": h.block_size, "cold": not args.hot}
         if wl.kind == "fused_topk":
             config["k"] = wl.k
     else:
-        config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": h.H, "head_dim": 128,
+        config = {"workload": wl.cfg["name"], "M": h.M, "N": h.N, "heads": h.H, "head_dim": h.D,
                   "cold": not args.hot}
     line = {
         "metric": "decode essential HBM TB/s (% of 8 TB/s); prefill fp8 TFLOP/s; us/call",

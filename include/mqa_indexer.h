@@ -81,11 +81,12 @@ typedef struct mqa_tunables {
  * Support gate (both pages, "Technical Details": callers ask before routing a
  * shape to these kernels and go elsewhere instead of failing).  Supported:
  * num_heads 32, 64 or 128 (the head counts the issue page about next_n tiling
- * sweeps) with head_dim 128, and for prefill also head_dim 64 (the head dims
- * of the aiter PR 5046 page's test sweep, "Test Plan").  kv_block_size: 0 asks
- * about prefill; 1, 16, 64 or 128 about paged decode with blocks of that many
- * tokens (at every head count).  Returns 1 if the current HIP device is gfx950
- * and the shape is supported, else 0.  Never fails.
+ * sweeps) with head_dim 128 or 64 (the head dims of the aiter PR 5046 page's
+ * test sweep, "Test Plan").  kv_block_size: 0 asks about prefill; 1, 16, 64 or
+ * 128 about paged decode with blocks of that many tokens (at every head
+ * count; head_dim 64 needs blocks of 16 or more tokens).  Returns 1 if the
+ * current HIP device is gfx950 and the shape is supported, else 0.  Never
+ * fails.
  */
 int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
 
@@ -164,9 +165,11 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * Entries past that are never read.  Scales must be >= 0.  Cache slots past a
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
- * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads (ring_depth tunable
- * other than 4 only with kv_block_size 64 and 32 heads).  kv_layout MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED (the
- * latter not with kv_block_size 1).
+ * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads and head_dim 128;
+ * head_dim 64 with kv_block_size 16, 64 or 128 (a block of bs tokens is then
+ * bs * 68 bytes).  The ring_depth tunable may differ from 4 only with
+ * kv_block_size 64, 32 heads and head_dim 128.  kv_layout MQA_KV_SLOT_MAJOR
+ * or MQA_KV_PRESHUFFLED (the latter not with kv_block_size 1).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
  * a bad kv_layout, negative sizes, NULL or misaligned pointers ->
  * MQA_ERR_INVALID_ARG; a shape, block size or layout outside the gate ->
@@ -224,7 +227,8 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  * (its logits into its workspace segment, then an exact radix select), so the
  * output is exact for every input; such rows only take longer.
  * Supported: every head count, block size and kv_layout that
- * paged_mqa_logits_decode takes; the ring_depth tunable 0 or the logits
+ * paged_mqa_logits_decode takes at head_dim 128 (head_dim 64 ->
+ * MQA_ERR_UNSUPPORTED); the ring_depth tunable 0 or the logits
  * call's default (3 for 64-token blocks at 32 heads, else 4); a KV split of
  * at most 1024.  Errors as for paged_mqa_logits_decode (a shape outside its
  * gate -> MQA_ERR_UNSUPPORTED, checked first), plus: k out of range, another

@@ -79,15 +79,16 @@ int check_device()
     return MQA_OK;
 }
 
-// 32, 64 or 128 index heads (the pages sweep all three); head dim 128, or 64
-// for prefill (the prefill page's test sweep covers head dims 64 and 128, the
-// decode page's only 128); cache blocks of 1, 16, 64 or 128 tokens for decode
-// (0 asks about prefill), at every head count.
+// 32, 64 or 128 index heads (the pages sweep all three); head dim 128 or 64
+// (the prefill page's test sweep covers head dims 64 and 128, the decode
+// page's only 128; the decode takes 64 too, in blocks of 16 or more tokens);
+// cache blocks of 1, 16, 64 or 128 tokens for decode (0 asks about prefill),
+// at every head count.
 bool shape_supported(int num_heads, int head_dim, int kv_block_size)
 {
     if (num_heads != 32 && num_heads != 64 && num_heads != 128)
         return false;
-    if (head_dim != 128 && !(head_dim == 64 && kv_block_size == 0))
+    if (head_dim != 128 && !(head_dim == 64 && kv_block_size != 1))
         return false;
     return kv_block_size == 0 || kv_block_size == 1 || kv_block_size == 16 ||
            kv_block_size == 64 || kv_block_size == 128;
@@ -229,8 +230,9 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
                     "(got %d)", kv_layout);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "decode supports num_heads 32, 64 or 128, head_dim 128 and kv_block_size 1, "
-                    "16, 64 or 128 (got %d, %d, %d)",
+                    "decode supports num_heads 32, 64 or 128, head_dim 128 with kv_block_size "
+                    "1, 16, 64 or 128, or head_dim 64 with kv_block_size 16, 64 or 128 "
+                    "(got %d, %d, %d)",
                     num_heads, head_dim, kv_block_size);
     if (kv_layout == MQA_KV_PRESHUFFLED && kv_block_size < 16)
         return fail(MQA_ERR_UNSUPPORTED, "the preshuffled layout needs kv_block_size 16, 64 or 128 "
@@ -240,13 +242,13 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
         t = *tun;
     const int head_tiles = num_heads / 32;
     const int max_rows = 4 / head_tiles;  // Q and weights of a wave's rows stay in VGPRs
-    const bool any_depth = kv_block_size == 64 && head_tiles == 1;
+    const bool any_depth = kv_block_size == 64 && head_tiles == 1 && head_dim == 128;
     if (t.rows_per_block < 0 || t.rows_per_block > max_rows || t.split_kv < 0 ||
         t.num_warps != 0 || t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7 ||
         (!any_depth && t.ring_depth != 0 && t.ring_depth != 4))
         return fail(MQA_ERR_INVALID_ARG,
                     "decode tunables: rows_per_block in 0..%d, split_kv >= 0, ring_depth 0 or 2..7 "
-                    "(0 or 4 unless 32 heads and kv_block_size 64), num_warps 0",
+                    "(0 or 4 unless 32 heads, head_dim 128 and kv_block_size 64), num_warps 0",
                     max_rows);
     if (batch == 0 || max_model_len == 0)
         return kNoop;
@@ -294,6 +296,7 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     int rows = t.rows_per_block ? t.rows_per_block : rows_default;
     rows = std::min(std::min(rows, next_n), max_rows);
     p.head_tiles = head_tiles;
+    p.head_dim = head_dim;
     p.rows = rows;
     //   short contexts (at most 128 steps): one step per workgroup, with a
     //   2-step ring (B 16, 8192 tokens: 6.6 -> 6.2 us).
@@ -360,10 +363,11 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
 {
     if (k < 1 || k > mqa::kMaxTopK)
         return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
-    if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
+    if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0 ||
+        head_dim != 128)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "the fused top-k takes the decode's shapes: num_heads 32, 64 or 128, "
-                    "head_dim 128, kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)", num_heads,
+                    "the fused top-k takes the decode's shapes at head_dim 128: num_heads 32, 64 "
+                    "or 128, kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)", num_heads,
                     head_dim, kv_block_size);
     // the sample and filter modes are built for the logits call's default ring
     const int depth = (kv_block_size == 64 && num_heads == 32) ? 3 : 4;
@@ -467,7 +471,7 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
     if (k_dtype != MQA_DTYPE_FP32 && k_dtype != MQA_DTYPE_BF16)
         return fail(MQA_ERR_INVALID_ARG, "k_dtype must be MQA_DTYPE_FP32 or MQA_DTYPE_BF16 (got %d)",
                     k_dtype);
-    if (!shape_supported(32, head_dim, kv_block_size) || kv_block_size == 0)
+    if (!shape_supported(32, head_dim, kv_block_size) || kv_block_size == 0 || head_dim != 128)
         return fail(MQA_ERR_UNSUPPORTED,
                     "K-cache insert supports head_dim=128, kv_block_size 1, 16, 64 or 128 "
                     "(got %d, %d)",

@@ -49,19 +49,27 @@ namespace mqa {
 namespace {
 
 
-constexpr int kSlotBytes = kBlockBytes;  // ring slot: one 64-token step, K rows + scales
+// A ring slot holds one 64-token step: the K rows (DIM bytes each), then the
+// 64 scales.  The K rows arrive as 1 KiB chunks of 1024 / DIM rows each.
+template <int DIM>
+constexpr int slot_bytes() { return kStep * DIM + kStep * 4; }
+template <int DIM>
+constexpr int k_chunks() { return kStep * DIM / 1024; }
+template <int DIM>
+constexpr int rows_per_chunk() { return 1024 / DIM; }
+constexpr int kSlotBytes = slot_bytes<kDim>();  // 8448 bytes at head dim 128
 constexpr int kSampleChunks = kFusedSampleChunks;
 constexpr int kSampleSteps = kFusedSampleSteps;
 constexpr int kSampleCols = kFusedSampleCols;
 
 // LDS bytes of a workgroup's ring (and, for per-token blocks, its table
 // ring).
-template <int D, int BS>
+template <int D, int BS, int DIM>
 constexpr int ring_lds_bytes()
 {
-    return D * kSlotBytes + (BS == 1 ? (2 * D - 2) * kStep * 4 : 0);
+    return D * slot_bytes<DIM>() + (BS == 1 ? (2 * D - 2) * kStep * 4 : 0);
 }
-constexpr int kChunks = kDim * kBlock / 1024 + 1;  // 8 x 1 KiB of K + 1 x 256 B of scales
+constexpr int kChunks = k_chunks<kDim>() + 1;  // 8 x 1 KiB of K + 1 x 256 B of scales
 
 // Sizes and launch shape; the pointers are separate __restrict__ kernel
 // arguments so the compiler may read the block table with scalar loads.
@@ -131,11 +139,11 @@ struct StepBlocks {
 
 constexpr int entries_per_step(int bs) { return bs >= kStep ? 1 : kStep / bs; }
 
-template <int BS>
+template <int BS, int DIM = kDim>
 struct Gather {
     static_assert(BS == 16 || BS == 64 || BS == 128, "block sizes with whole chunks");
-    static constexpr int kEntries = entries_per_step(BS);        // table entries per step
-    static constexpr int64_t kBytes = (int64_t)BS * (kDim + 4);  // bytes per block
+    static constexpr int kEntries = entries_per_step(BS);       // table entries per step
+    static constexpr int64_t kBytes = (int64_t)BS * (DIM + 4);  // bytes per block
 
     struct Src {
         StepBlocks<kEntries> blk;
@@ -168,28 +176,30 @@ struct Gather {
 // Request a step into ring slot `slot` (wave g of G; see Gather): blk_of and
 // off are the fields of the step's Gather<BS>::Src (passed by value, so the
 // pointers stay in registers).
-template <int G, int BS>
+template <int G, int BS, int DIM = kDim>
 __device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_per_step(BS)> blk_of,
                                              int off, bool tiled, int g, int lane)
 {
     constexpr int kEntries = entries_per_step(BS);
-    constexpr int KC = kChunks - 1;
+    constexpr int KC = k_chunks<DIM>();
+    constexpr int TPC = rows_per_chunk<DIM>();
     constexpr int J = (KC + G - 1) / G;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int c = g + G * j;
         if (G * J == KC || c < KC) {
-            const int q = lane ^ (8 * (c & 1));
-            const int e = BS >= kStep ? 0 : (8 * c) / BS;  // wave-uniform
+            // granule q = TPC u + tau: 16-byte granule u of chunk row tau
+            const int q = DIM == 128 ? lane ^ (8 * (c & 1)) : lane;
+            const int e = BS >= kStep ? 0 : (TPC * c) / BS;  // wave-uniform
             const uint8_t *blk = blk_of.p[0];
 #pragma unroll
             for (int i = 1; i < kEntries; ++i)  // selects, not a dynamic index
                 if (e == i)
                     blk = blk_of.p[i];
-            const int row = (BS >= kStep ? off + 8 * c : (8 * c) % BS) + (q & 7);
-            const int u = q >> 3;
-            const int src = tiled ? (row >> 4) * (16 * kDim) + u * 256 + (row & 15) * 16
-                                  : row * kDim + u * 16;
+            const int row = (BS >= kStep ? off + TPC * c : (TPC * c) % BS) + q % TPC;
+            const int u = q / TPC;
+            const int src = tiled ? (row >> 4) * (16 * DIM) + u * 256 + (row & 15) * 16
+                                  : row * DIM + u * 16;
             __builtin_amdgcn_global_load_lds(blk + src, slot + 1024 * c, 16, 0, kStreamHint);
         }
     }
@@ -203,7 +213,7 @@ __device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_pe
                     blk = blk_of.p[e];
             row = lane % BS;
         }
-        __builtin_amdgcn_global_load_lds(blk + BS * kDim + row * 4, slot + kBlock * kDim, 4, 0,
+        __builtin_amdgcn_global_load_lds(blk + BS * DIM + row * 4, slot + kStep * DIM, 4, 0,
                                          kStreamHint);
     }
 }
@@ -267,13 +277,14 @@ __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, c
 }
 
 // The fewest global->LDS loads any wave of G issues per step, with
-// loads_per_chunk loads per K chunk and the scale load on the last wave.
-constexpr int min_loads_per_step(int G, int loads_per_chunk)
+// loads_per_chunk loads per each of kchunks K chunks and the scale load on the
+// last wave.
+constexpr int min_loads_per_step(int G, int loads_per_chunk, int kchunks)
 {
     int m = 1 << 30;
     for (int g = 0; g < G; ++g) {
         int n = g == G - 1 ? 1 : 0;
-        for (int c = g; c < kChunks - 1; c += G)
+        for (int c = g; c < kchunks; c += G)
             n += loads_per_chunk;
         m = n < m ? n : m;
     }
@@ -288,46 +299,69 @@ __device__ __forceinline__ void wait_vm()
 }
 
 
-// Read a ring slot into registers.  Lane (t, g') needs token 32 h + t,
-// granules u = 2j + g', j = 0..3: chunk c = 4h + t/8 (same parity for both
-// tiles), logical granule q = 16 j + 8 g' + t % 8, stored at position
+// Read a ring slot into registers (head dim 128).  Lane (t, g') needs token
+// 32 h + t, granules u = 2j + g', j = 0..3: chunk c = 4h + t/8 (same parity
+// for both tiles), logical granule q = 16 j + 8 g' + t % 8, stored at position
 // q ^ 8 (c & 1) = 16 j + 8 (g' ^ (c & 1)) + t % 8, so read j sits 256 bytes
-// after read 0.  The reads are inline asm because the compiler would
-// otherwise make every LDS read wait for all outstanding global->LDS loads;
-// read_wait() completes them.
-__device__ __forceinline__ void read_block(KStep &k, uint32_t slot, int lane)
+// after read 0.  Head dim 64: chunk c = 2h + t/16 holds rows 16c..16c+15
+// unswizzled (granule u of row tau at position 16 u + tau), lane (t, g') reads
+// u = 2j + g', j = 0, 1, at position 32 j + 16 g' + t % 16; each 16-lane pass
+// of ds_read_b128 then reads 256 contiguous bytes, all 64 banks once.  The
+// reads are inline asm because the compiler would otherwise make every LDS
+// read wait for all outstanding global->LDS loads; read_wait() completes them.
+template <int DIM>
+__device__ __forceinline__ void read_block(KStepOf<DIM> &k, uint32_t slot, int lane)
 {
     const int t = lane & 31, gq = lane >> 5;
-    const int c = t >> 3;  // chunk within the tile; tile 1 adds 4 (same parity)
-    const int p0 = 8 * (gq ^ (c & 1)) + (t & 7);
-    const uint32_t a0 = slot + (c * 1024 + p0 * 16);
-    const uint32_t a1 = a0 + 4096;
-    const uint32_t sa = slot + kBlock * kDim + t * 4;
-    asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[0].c[0]) : "v"(a0));
-    asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(k.t[0].c[1]) : "v"(a0));
-    asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[0].c[2]) : "v"(a0));
-    asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(k.t[0].c[3]) : "v"(a0));
-    asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[1].c[0]) : "v"(a1));
-    asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(k.t[1].c[1]) : "v"(a1));
-    asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[1].c[2]) : "v"(a1));
-    asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(k.t[1].c[3]) : "v"(a1));
+    const uint32_t sa = slot + kStep * DIM + t * 4;
+    if constexpr (DIM == 128) {
+        const int c = t >> 3;  // chunk within the tile; tile 1 adds 4 (same parity)
+        const int p0 = 8 * (gq ^ (c & 1)) + (t & 7);
+        const uint32_t a0 = slot + (c * 1024 + p0 * 16);
+        const uint32_t a1 = a0 + 4096;
+        asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[0].c[0]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(k.t[0].c[1]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[0].c[2]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(k.t[0].c[3]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[1].c[0]) : "v"(a1));
+        asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(k.t[1].c[1]) : "v"(a1));
+        asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[1].c[2]) : "v"(a1));
+        asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(k.t[1].c[3]) : "v"(a1));
+    } else {
+        static_assert(DIM == 64, "head dim 64 or 128");
+        const uint32_t a0 = slot + (t >> 4) * 1024 + (16 * gq + (t & 15)) * 16;
+        const uint32_t a1 = a0 + 2048;
+        asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[0].c[0]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[0].c[1]) : "v"(a0));
+        asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(k.t[1].c[0]) : "v"(a1));
+        asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(k.t[1].c[1]) : "v"(a1));
+    }
     asm volatile("ds_read_b32 %0, %1 offset:0" : "=v"(k.sc[0]) : "v"(sa));
     asm volatile("ds_read_b32 %0, %1 offset:128" : "=v"(k.sc[1]) : "v"(sa));
 }
 
 // Wait for read_block's results; the registers pass through the asm, so no
 // use of them can be scheduled before the wait.
-__device__ __forceinline__ void read_wait(KStep &k)
+template <int DIM>
+__device__ __forceinline__ void read_wait(KStepOf<DIM> &k)
 {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(k.t[0].c[0]), "+v"(k.t[0].c[1]), "+v"(k.t[0].c[2]), "+v"(k.t[0].c[3]),
-                   "+v"(k.t[1].c[0]), "+v"(k.t[1].c[1]), "+v"(k.t[1].c[2]), "+v"(k.t[1].c[3]),
-                   "+v"(k.sc[0]), "+v"(k.sc[1])
-                 :
-                 : "memory");
+    if constexpr (DIM == 128) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(k.t[0].c[0]), "+v"(k.t[0].c[1]), "+v"(k.t[0].c[2]), "+v"(k.t[0].c[3]),
+                       "+v"(k.t[1].c[0]), "+v"(k.t[1].c[1]), "+v"(k.t[1].c[2]), "+v"(k.t[1].c[3]),
+                       "+v"(k.sc[0]), "+v"(k.sc[1])
+                     :
+                     : "memory");
+    } else {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(k.t[0].c[0]), "+v"(k.t[0].c[1]), "+v"(k.t[1].c[0]), "+v"(k.t[1].c[1]),
+                       "+v"(k.sc[0]), "+v"(k.sc[1])
+                     :
+                     : "memory");
+    }
 }
 
-template <int R, int G, int D, int BS, int HT, int MODE = kLogits>
+template <int R, int G, int D, int BS, int HT, int MODE = kLogits, int DIM = kDim>
 __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restrict__ qbuf,
                                                         const uint8_t *__restrict__ cache,
                                                         const float *__restrict__ wbuf,
@@ -370,7 +404,9 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
 
     if (st0 < st1) {
         constexpr int H = kHeads * HT;
-        Frag q[R][HT];
+        static_assert(DIM == kDim || (BS != 1 && MODE == kLogits),
+                      "head dim 64: blocks of 16 or more tokens, logits only");
+        Operand<DIM> q[R][HT];
         Weights16 w[R][HT];
         // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f)
         // and the entries kept so far for it (each row belongs to one wave, and
@@ -392,7 +428,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
             const int64_t row = row_base + min(r, nrows - 1);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                load_frag(q[r][ht], qbuf + row * (H * kDim) + (ht * kHeads + t) * kDim, lane);
+                load_frag(q[r][ht], qbuf + row * (H * DIM) + (ht * kHeads + t) * DIM, lane);
                 load_weights(w[r][ht], wbuf + row * H + ht * kHeads, lane);
             }
         }
@@ -473,7 +509,8 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         const bool tiled = a.tiled != 0;
         lds_u8 *ring = (lds_u8 *)ring_mem;
         const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-        using Gth = Gather<(BS == 1 ? kBlock : BS)>;  // unused for BS = 1
+        using Gth = Gather<(BS == 1 ? kBlock : BS), DIM>;  // unused for BS = 1
+        constexpr int SB = slot_bytes<DIM>();
         const int last_entry = (nvalid - 1) / BS;
         // BS = 1: table ring of 2D - 2 steps of 64 entries after the K ring.
         // Entries for step y are loaded (by wave 0) in the iteration that
@@ -481,8 +518,8 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         // iteration that requests step y: by then the wait for step
         // y - D + 1 has covered them, and the barrier published them.
         constexpr int kTabSlots = 2 * D - 2;
-        lds_u8 *tring = ring + D * kSlotBytes;
-        const uint32_t tring_addr = ring_addr + D * kSlotBytes;
+        lds_u8 *tring = ring + D * SB;
+        const uint32_t tring_addr = ring_addr + D * SB;
         auto request_table = [&](int y) {  // wave 0 only
             const int tok = min(y * kStep + lane, last_entry);
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(table + tok),
@@ -501,14 +538,14 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
 #pragma unroll
             for (int i = 0; i < D - 1; ++i)
                 if (st0 + i < st1)
-                    request_tokens<G>(ring + i * kSlotBytes, tring_addr + i * (kStep * 4), cache, g,
+                    request_tokens<G>(ring + i * SB, tring_addr + i * (kStep * 4), cache, g,
                                       lane);
         } else {
 #pragma unroll
             for (int i = 0; i < D - 1; ++i)
                 if (st0 + i < st1) {
                     const typename Gth::Src src = Gth::fetch(cache, table, st0 + i, last_entry);
-                    request_step<G, BS>(ring + i * kSlotBytes, src.blk, src.off, tiled, g, lane);
+                    request_step<G, BS, DIM>(ring + i * SB, src.blk, src.off, tiled, g, lane);
                 }
         }
         // Between requesting block k and waiting for it a wave requests the
@@ -518,7 +555,8 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         // well only make the wait stricter).  In the last D - 2 steps fewer
         // blocks follow and the wave waits for everything.
         // (vmcnt holds at most 63; a smaller count is a stricter wait)
-        constexpr int kWaitRaw = (D - 2) * min_loads_per_step(G, BS == 1 ? kTokLoadsPerChunk : 1);
+        constexpr int kWaitRaw =
+            (D - 2) * min_loads_per_step(G, BS == 1 ? kTokLoadsPerChunk : 1, k_chunks<DIM>());
         constexpr int kWait = kWaitRaw < 63 ? kWaitRaw : 63;
         int rd = 0;      // slot of step st
         int wr = D - 1;  // slot of step st + D - 1
@@ -541,23 +579,23 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                 if (g == 0 && st + kTabSlots < st1)
                     request_table(st + kTabSlots);
                 if (st + D - 1 < st1)
-                    request_tokens<G>(ring + wr * kSlotBytes,
+                    request_tokens<G>(ring + wr * SB,
                                       tring_addr + ((st + D - 1 - st0) % kTabSlots) * (kStep * 4),
                                       cache, g, lane);
             } else {
                 if (st + D - 1 < st1)
-                    request_step<G, BS>(ring + wr * kSlotBytes, next.blk, next.off, tiled, g,
+                    request_step<G, BS, DIM>(ring + wr * SB, next.blk, next.off, tiled, g,
                                         lane);
                 next = Gth::fetch(cache, table, min(st + D, st1 - 1), last_entry);
             }
-            KStep kb;
-            read_block(kb, ring_addr + rd * kSlotBytes, lane);
+            KStepOf<DIM> kb;
+            read_block<DIM>(kb, ring_addr + rd * SB, lane);
             if (st > st0)
                 store_step(st - 1, prev_tot);
             rd = (rd + 1 == D) ? 0 : rd + 1;
             wr = (wr + 1 == D) ? 0 : wr + 1;
-            read_wait(kb);
-            step_scores<R, HT>(kb, q, w, prev_tot);
+            read_wait<DIM>(kb);
+            step_scores<R, HT, DIM>(kb, q, w, prev_tot);
         }
         store_step(st1 - 1, prev_tot);
         if constexpr (MODE == kFilter) {
@@ -592,27 +630,29 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
     }
 }
 
-template <int R, int G, int D, int BS, int HT = 1, int MODE = kLogits>
+template <int R, int G, int D, int BS, int HT = 1, int MODE = kLogits, int DIM = kDim>
 hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
-    const size_t lds = (size_t)ring_lds_bytes<D, BS>();
-    hipLaunchKernelGGL((decode_kernel<R, G, D, BS, HT, MODE>), dim3(grid), dim3(64 * G), lds, stream,
-                       p.q, p.cache, p.weights, p.context_lens, p.block_tables, p.logits, a);
+    const size_t lds = (size_t)ring_lds_bytes<D, BS, DIM>();
+    hipLaunchKernelGGL((decode_kernel<R, G, D, BS, HT, MODE, DIM>), dim3(grid), dim3(64 * G), lds,
+                       stream, p.q, p.cache, p.weights, p.context_lens, p.block_tables, p.logits,
+                       a);
     return hipGetLastError();
 }
 
-// The kernels a (rows per wave R, waves G, head tiles HT, mode) launch can
-// take, by block size and ring depth: 64-token blocks at 32 heads take ring
-// depths 2..7 for the logits call and 3 for the fused top-k's modes; every
-// other layout takes depth 4.  (Q and weights of a wave's rows stay in VGPRs,
-// so R HT <= 4.)
-template <int R, int G, int HT, int MODE>
+// The kernels a (rows per wave R, waves G, head tiles HT, mode, head dim)
+// launch can take, by block size and ring depth: 64-token blocks at 32 heads
+// and head dim 128 take ring depths 2..7 for the logits call and 3 for the
+// fused top-k's modes; every other layout takes depth 4, and head dim 64
+// blocks of 16 or more tokens.  (Q and weights of a wave's rows stay in
+// VGPRs, so R HT <= 4.)
+template <int R, int G, int HT, int MODE, int DIM = kDim>
 hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
     if constexpr (R * HT > 4) {
         return hipErrorInvalidValue;
     } else {
-        if constexpr (HT == 1) {
+        if constexpr (HT == 1 && DIM == kDim) {
             if (p.block_size == 64) {
                 if constexpr (MODE == kLogits) {
                     switch (p.depth) {
@@ -633,41 +673,45 @@ hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipSt
         if (p.depth != 4)
             return hipErrorInvalidValue;
         switch (p.block_size) {
-        case 1: return launch_rgdb<R, G, 4, 1, HT, MODE>(p, a, grid, stream);
-        case 16: return launch_rgdb<R, G, 4, 16, HT, MODE>(p, a, grid, stream);
+        case 1:
+            if constexpr (DIM == kDim)
+                return launch_rgdb<R, G, 4, 1, HT, MODE>(p, a, grid, stream);
+            else
+                return hipErrorInvalidValue;
+        case 16: return launch_rgdb<R, G, 4, 16, HT, MODE, DIM>(p, a, grid, stream);
         case 64:
-            if constexpr (HT > 1)
-                return launch_rgdb<R, G, 4, 64, HT, MODE>(p, a, grid, stream);
+            if constexpr (HT > 1 || DIM != kDim)
+                return launch_rgdb<R, G, 4, 64, HT, MODE, DIM>(p, a, grid, stream);
             else
                 return hipErrorInvalidValue;  // handled above
-        case 128: return launch_rgdb<R, G, 4, 128, HT, MODE>(p, a, grid, stream);
+        case 128: return launch_rgdb<R, G, 4, 128, HT, MODE, DIM>(p, a, grid, stream);
         default: return hipErrorInvalidValue;
         }
     }
 }
 
 // (rows, row groups) pairs that next_n in 1..8 can produce
-template <int HT, int MODE>
+template <int HT, int MODE, int DIM = kDim>
 hipError_t launch_ht(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
     switch (p.rows * 16 + a.groups) {
-    case 1 * 16 + 1: return launch_rg<1, 1, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 2: return launch_rg<1, 2, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 3: return launch_rg<1, 3, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 4: return launch_rg<1, 4, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 5: return launch_rg<1, 5, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 6: return launch_rg<1, 6, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 7: return launch_rg<1, 7, HT, MODE>(p, a, grid, stream);
-    case 1 * 16 + 8: return launch_rg<1, 8, HT, MODE>(p, a, grid, stream);
-    case 2 * 16 + 1: return launch_rg<2, 1, HT, MODE>(p, a, grid, stream);
-    case 2 * 16 + 2: return launch_rg<2, 2, HT, MODE>(p, a, grid, stream);
-    case 2 * 16 + 3: return launch_rg<2, 3, HT, MODE>(p, a, grid, stream);
-    case 2 * 16 + 4: return launch_rg<2, 4, HT, MODE>(p, a, grid, stream);
-    case 3 * 16 + 1: return launch_rg<3, 1, HT, MODE>(p, a, grid, stream);
-    case 3 * 16 + 2: return launch_rg<3, 2, HT, MODE>(p, a, grid, stream);
-    case 3 * 16 + 3: return launch_rg<3, 3, HT, MODE>(p, a, grid, stream);
-    case 4 * 16 + 1: return launch_rg<4, 1, HT, MODE>(p, a, grid, stream);
-    case 4 * 16 + 2: return launch_rg<4, 2, HT, MODE>(p, a, grid, stream);
+    case 1 * 16 + 1: return launch_rg<1, 1, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 2: return launch_rg<1, 2, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 3: return launch_rg<1, 3, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 4: return launch_rg<1, 4, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 5: return launch_rg<1, 5, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 6: return launch_rg<1, 6, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 7: return launch_rg<1, 7, HT, MODE, DIM>(p, a, grid, stream);
+    case 1 * 16 + 8: return launch_rg<1, 8, HT, MODE, DIM>(p, a, grid, stream);
+    case 2 * 16 + 1: return launch_rg<2, 1, HT, MODE, DIM>(p, a, grid, stream);
+    case 2 * 16 + 2: return launch_rg<2, 2, HT, MODE, DIM>(p, a, grid, stream);
+    case 2 * 16 + 3: return launch_rg<2, 3, HT, MODE, DIM>(p, a, grid, stream);
+    case 2 * 16 + 4: return launch_rg<2, 4, HT, MODE, DIM>(p, a, grid, stream);
+    case 3 * 16 + 1: return launch_rg<3, 1, HT, MODE, DIM>(p, a, grid, stream);
+    case 3 * 16 + 2: return launch_rg<3, 2, HT, MODE, DIM>(p, a, grid, stream);
+    case 3 * 16 + 3: return launch_rg<3, 3, HT, MODE, DIM>(p, a, grid, stream);
+    case 4 * 16 + 1: return launch_rg<4, 1, HT, MODE, DIM>(p, a, grid, stream);
+    case 4 * 16 + 2: return launch_rg<4, 2, HT, MODE, DIM>(p, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -339,6 +339,9 @@ CONFIGS = {
              ctx=131072, mml=131072, H=64, block_size=128),
     20: dict(kind="decode", name="decode_B16_nn6_ctx131072_h128_bs128", B=16, next_n=6,
              ctx=131072, mml=131072, H=128, block_size=128),
+    # the headline decode shape at head dim 64 (64-byte K rows)
+    21: dict(kind="decode", name="decode_B16_nn6_ctx131072_d64", B=16, next_n=6, ctx=131072,
+             mml=131072, D=64),
 }
 
 
@@ -351,7 +354,7 @@ def make_config(idx: int, poison: bool = False):
     return make_decode(c["B"], c["next_n"], c["ctx"], c["mml"], seed,
                        ctx_range=c.get("ctx_range"), poison=poison,
                        block_size=c.get("block_size", KV_BLOCK), H=c.get("H", HEADS),
-                       preshuffle=c.get("preshuffle", False))
+                       D=c.get("D", HEAD_DIM), preshuffle=c.get("preshuffle", False))
 
 
 # Row families for the top-k over logits: shapes a logits row takes (a masked

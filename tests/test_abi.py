@@ -121,7 +121,14 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls, bs=16) == mqa._native.MQA_ERR_INVALID_ARG  # supported; NULLs
     assert _decode(lib, nulls, bs=0) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, H=48) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert _decode(lib, nulls, D=64) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, D=96) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert _decode(lib, nulls, D=64, bs=1) == mqa._native.MQA_ERR_UNSUPPORTED
+    for bs in (16, 64, 128):  # head dim 64: blocks of 16 or more tokens
+        assert _decode(lib, nulls, D=64, bs=bs) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
+        assert "NULL" in mqa.last_error()
+    bad = _native.Tunables(ring_depth=3)  # head dim 64: ring depth 0 or 4
+    assert _decode(lib, nulls, D=64, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "ring_depth" in mqa.last_error()
     for H in (64, 128):
         for bs in (1, 16, 128):
             assert _decode(lib, nulls, H=H, bs=bs) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs

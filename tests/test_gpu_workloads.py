@@ -61,7 +61,7 @@ def test_prefill_workload(idx):
     assert_parity(out[rows], ref, mag, f"workload{idx}")
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20])
+@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20, 21])
 def test_decode_workload(idx):
     t0 = time.time()
     d = inputs.make_config(idx, poison=True)

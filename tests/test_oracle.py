@@ -163,6 +163,7 @@ def test_prefill_matches_exact_brute_force(H, D, M, N, mode):
 @pytest.mark.parametrize("H,D,B,next_n,bs,ctx", [
     (2, 4, 2, 2, 4, [5, 9]),
     (32, 128, 1, 3, 64, [70]),
+    (2, 64, 2, 2, 16, [20, 33]),
     (3, 8, 3, 3, 2, [0, 2, 7]),
     (1, 1, 2, 1, 8, [17, 3]),
 ])
@@ -252,17 +253,18 @@ def test_hoisted_scale_equals_unhoisted():
     assert np.max(np.abs(a[fin] - b[fin])) <= 1e-14 * np.max(np.abs(a[fin]))
 
 
-def test_paged_decode_equals_contiguous_prefill():
+@pytest.mark.parametrize("D", [128, 64])
+def test_paged_decode_equals_contiguous_prefill(D):
     """Row (b, j) of decode = prefill over that sequence's gathered K with
     ks = 0, ke = ctx_b - next_n + j + 1, and -inf out to max_model_len."""
     B, next_n, mml = 3, 4, 300
-    d = inputs.make_decode(B, next_n, [250, 3, 129], mml, seed=41, poison=True)
+    d = inputs.make_decode(B, next_n, [250, 3, 129], mml, seed=41, D=D, poison=True)
     dec = oracle.decode(d.q, d.kv_cache, d.weights, d.context_lens, d.block_tables, mml, 64)
     for b in range(B):
         ctx = int(d.context_lens[b])
         for j in range(next_n):
             row = b * next_n + j
-            k = d.k_seq[b] if ctx else np.zeros((1, 128), np.uint8)
+            k = d.k_seq[b] if ctx else np.zeros((1, D), np.uint8)
             sc = d.s_seq[b] if ctx else np.ones(1, np.float32)
             N = k.shape[0]
             pre = oracle.prefill(d.q[b, j][None], k, sc, d.weights[row][None],
@@ -390,13 +392,14 @@ def test_generator_preshuffle_matches_hand_positions(row):
     assert int(np.flatnonzero(tiled[0])[0]) == offset and int(tiled.sum()) == 1
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("bs", [16, 64, 128])
-def test_preshuffled_decode_equals_plain_decode(bs):
+def test_preshuffled_decode_equals_plain_decode(bs, D):
     """Invariant: the layout moves bytes, not values, so the oracle's logits on
     the preshuffled cache equal those on the slot-major cache of the same
     draws, bit for bit (ragged contexts, shuffled table, NaN-poisoned slots)."""
     kw = dict(B=3, next_n=3, context_lens=[5, bs + 7, 2 * bs], max_model_len=2 * bs + 8, seed=77,
-              H=4, block_size=bs, poison=True)
+              H=4, D=D, block_size=bs, poison=True)
     a = inputs.make_decode(**kw)
     b = inputs.make_decode(preshuffle=True, **kw)
     assert not np.array_equal(a.kv_cache, b.kv_cache)
@@ -417,3 +420,33 @@ def test_preshuffle_needs_whole_tiles():
     with pytest.raises(ValueError):
         oracle.decode(q, cache, np.ones((1, 1), np.float32), np.array([8], np.int32),
                       np.zeros((1, 1), np.int32), 8, 8, preshuffle=True)
+
+
+# Hand-worked byte offsets of the preshuffled order at head dim 64 (16 rows of
+# 64 bytes per tile group: a group is 1024 bytes, granule u of its 16 rows
+# takes bytes 256 u .. 256 u + 255, row by row):
+#   slot 0, byte 0   -> 0
+#   slot 3, byte 17  -> granule 1, row 3: 256 + 48 + 1 = 305
+#   slot 15, byte 63 -> granule 3, row 15: 768 + 240 + 15 = 1023
+#   slot 17, byte 5  -> group 1 (1024), granule 0, row 1: 1024 + 16 + 5 = 1045
+#   slot 33, byte 40 -> group 2 (2048), granule 2, row 1: 2048 + 512 + 16 + 8 = 2584
+D64_TILED_POSITIONS = [(0, 0, 0), (3, 17, 305), (15, 63, 1023), (17, 5, 1045), (33, 40, 2584)]
+
+
+@pytest.mark.parametrize("slot,byte,pos", D64_TILED_POSITIONS)
+def test_preshuffle_positions_head_dim_64(slot, byte, pos):
+    """The generator's preshuffled order at head dim 64 puts byte `byte` of
+    slot `slot` at the hand-worked position, and the oracle reads it back from
+    there: a one-hot K byte gives a logit only at that slot."""
+    bs, D = 64, 64
+    cache = np.zeros((1, bs * (D + 4)), np.uint8)
+    k = cache[:, : bs * D].reshape(1, bs, D)
+    k[0, slot, byte] = 0x38  # 1.0
+    tiled = inputs.preshuffle_blocks(cache, bs, D)
+    assert tiled[0, pos] == 0x38 and int(np.count_nonzero(tiled[0, : bs * D])) == 1
+    tiled[0, bs * D:] = np.ones(bs, np.float32).view(np.uint8)  # unit scales
+    q = np.zeros((1, 1, 1, D), np.uint8)
+    q[0, 0, 0, byte] = 0x38
+    out = oracle.decode(q, tiled, np.ones((1, 1), np.float32), np.array([bs], np.int32),
+                        np.zeros((1, 1), np.int32), bs, bs, preshuffle=True)
+    assert out[0, slot] == 1.0 and np.count_nonzero(out[0]) == 1
