@@ -265,15 +265,15 @@ size_t paged_mqa_topk_workspace_size(int batch, int next_n, int max_model_len);
  *
  * Per token: scale = fp32(max(amax, 1e-12) / 448) (one correctly rounded
  * division), codes = e4m3fn(clamp(k / scale, -448, 448)) rounded to nearest,
- * ties to even, sign kept.  The token's 128 code bytes and its scale are
+ * ties to even, sign kept.  The token's head_dim code bytes and its scale are
  * written to its slot; nothing else in the cache changes.  Slots at or past
  * num_blocks * kv_block_size are skipped as well.  Two tokens mapped to the
  * same slot race (either may win).
  * num_tokens == 0 is a successful no-op.  Negative sizes, a bad k_dtype or
  * kv_layout, NULL or misaligned pointers (k and kv_cache 16-byte,
- * slot_mapping 8-byte) -> MQA_ERR_INVALID_ARG; head_dim != 128, kv_block_size
- * not 1, 16, 64 or 128, or the preshuffled layout with kv_block_size 1 ->
- * MQA_ERR_UNSUPPORTED.
+ * slot_mapping 8-byte) -> MQA_ERR_INVALID_ARG; head_dim other than 128 or 64,
+ * kv_block_size not 1, 16, 64 or 128, head_dim 64 with kv_block_size 1, or the
+ * preshuffled layout with kv_block_size 1 -> MQA_ERR_UNSUPPORTED.
  */
 int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
                                uint8_t *kv_cache, int num_tokens, int head_dim,

@@ -471,9 +471,10 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
     if (k_dtype != MQA_DTYPE_FP32 && k_dtype != MQA_DTYPE_BF16)
         return fail(MQA_ERR_INVALID_ARG, "k_dtype must be MQA_DTYPE_FP32 or MQA_DTYPE_BF16 (got %d)",
                     k_dtype);
-    if (!shape_supported(32, head_dim, kv_block_size) || kv_block_size == 0 || head_dim != 128)
+    if (!shape_supported(32, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "K-cache insert supports head_dim=128, kv_block_size 1, 16, 64 or 128 "
+                    "K-cache insert supports head_dim 128 with kv_block_size 1, 16, 64 or 128, or "
+                    "head_dim 64 with kv_block_size 16, 64 or 128 "
                     "(got %d, %d)",
                     head_dim, kv_block_size);
     if (kv_layout != MQA_KV_SLOT_MAJOR && kv_layout != MQA_KV_PRESHUFFLED)
@@ -492,6 +493,7 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
         return rc;
     mqa::KcacheLaunch p;
     p.k = k;
+    p.head_dim = head_dim;
     p.slots = slot_mapping;
     p.cache = kv_cache;
     p.tokens = num_tokens;

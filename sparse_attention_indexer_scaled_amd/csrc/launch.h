@@ -130,9 +130,10 @@ struct FusedTopkLaunch {
 };
 
 struct KcacheLaunch {
-    const void *k;        // [tokens, 128] fp32 or bf16
+    const void *k;        // [tokens, head_dim] fp32 or bf16
     const int64_t *slots; // [tokens]
-    uint8_t *cache;       // [num_slots / block_size] blocks of block_size * 132 bytes
+    uint8_t *cache;       // [num_slots / block_size] blocks of block_size * (head_dim + 4) bytes
+    int head_dim;         // 128, or 64 (blocks of 16 or more tokens)
     int tokens;
     int block_size;
     int64_t num_slots;    // num_blocks * block_size

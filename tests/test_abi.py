@@ -221,7 +221,9 @@ def test_kcache_validation(lib):
     assert f(None, 0, None, None, -1, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert f(None, 2, None, None, 5, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert "k_dtype" in mqa.last_error()
-    assert f(None, 0, None, None, 5, 64, 64, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 5, 96, 64, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 5, 64, 1, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 5, 64, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
     assert f(None, 1, None, None, 5, 128, 32, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
     assert f(None, 0, None, None, 5, 128, 64, 3, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert "kv_layout" in mqa.last_error()

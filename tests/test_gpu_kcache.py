@@ -137,3 +137,38 @@ def test_zero_tokens_is_a_no_op():
                                    torch.empty((0,), dtype=torch.int64, device="cuda"), cache)
     torch.cuda.synchronize()
     assert int(cache.sum()) == 0
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("bs,pre", [(16, False), (64, False), (128, False), (16, True),
+                                    (64, True), (128, True)])
+def test_insert_head_dim_64(bs, pre, bf16):
+    """Head dim 64: 64 code bytes per token (one per lane), the scale after the
+    block's 64-byte rows; the whole cache equals the oracle's bit for bit."""
+    c = inputs.make_kcache_insert(900, -(-900 // bs) + 2, seed=660 + bs + bf16, block_size=bs, D=64,
+                                  bf16=bf16)
+    say("kcache insert d64 bs=%d preshuffle=%s bf16=%d" % (bs, pre, bf16))
+    got = gpu_insert(c, preshuffle=pre)
+    want = oracle_kcache.insert(c.kv_cache, c.k, c.slot_mapping, bs, preshuffle=pre)
+    if not np.array_equal(got, want):
+        diff = np.argwhere(got != want)
+        raise AssertionError("%d bytes differ, first at %s" % (len(diff), diff[0].tolist()))
+
+
+def test_insert_then_decode_end_to_end_head_dim_64():
+    """The insert-then-decode chain at head dim 64 (64-token blocks, 64 heads)."""
+    import dataclasses
+    d = inputs.make_decode(2, 3, [700, 1500], 1600, seed=614, H=64, D=64)
+    rng = np.random.default_rng(615)
+    slots = np.concatenate([d.block_tables[b, np.arange(int(d.context_lens[b])) // 64] * 64
+                            + np.arange(int(d.context_lens[b])) % 64 for b in range(d.B)])
+    k = (rng.standard_normal((slots.size, 64)) * 3).astype(np.float32)
+    empty = np.zeros_like(d.kv_cache)
+    say("kcache insert d64 feeding decode")
+    c = inputs.KcacheInsertInputs(k, slots.astype(np.int64), empty, 64, False)
+    gpu_cache = gpu_insert(c)
+    oracle_cache = oracle_kcache.insert(empty, k, slots, 64)
+    assert np.array_equal(gpu_cache, oracle_cache)
+    out = run_decode(dataclasses.replace(d, kv_cache=gpu_cache))
+    ref, mag, _ = oracle_decode(dataclasses.replace(d, kv_cache=oracle_cache))
+    assert_parity(out, ref, mag, "decode d64 after insert")

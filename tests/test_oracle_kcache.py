@@ -78,11 +78,12 @@ def test_matches_the_generators_quantiser():
     assert np.array_equal(codes, gcodes)
 
 
-def test_inserted_cache_feeds_the_decode_oracle():
+@pytest.mark.parametrize("D", [128, 64])
+def test_inserted_cache_feeds_the_decode_oracle(D):
     """Tokens quantised into a shuffled set of slots read back, through the
     decode oracle's own gather, as the prefill oracle on the same codes."""
     rng = np.random.default_rng(13)
-    bs, D, H = 64, 128, 32
+    bs, H = 64, 32
     T = 150
     nblocks = 4
     k = rng.standard_normal((T, D)).astype(np.float32)
@@ -127,12 +128,13 @@ def test_preshuffled_insert_positions_worked_by_hand():
         assert out[1, bs * D + 4 * slot: bs * D + 4 * slot + 4].view(np.float32)[0] == 1.0
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("bs", [16, 64, 128])
-def test_preshuffled_insert_is_the_permuted_plain_insert(bs):
+def test_preshuffled_insert_is_the_permuted_plain_insert(bs, D):
     """The generator's block permutation (numpy reshape/transpose) applied to
     the slot-major insert gives the preshuffled insert, byte for byte."""
-    d = inputs.make_kcache_insert(40, 4, seed=5, block_size=bs)
+    d = inputs.make_kcache_insert(40, 4, seed=5, block_size=bs, D=D)
     plain = kcache.insert(d.kv_cache, d.k, d.slot_mapping, bs)
-    tiled_prior = inputs.preshuffle_blocks(d.kv_cache, bs, 128)
+    tiled_prior = inputs.preshuffle_blocks(d.kv_cache, bs, D)
     tiled = kcache.insert(tiled_prior, d.k, d.slot_mapping, bs, preshuffle=True)
-    assert np.array_equal(tiled, inputs.preshuffle_blocks(plain, bs, 128))
+    assert np.array_equal(tiled, inputs.preshuffle_blocks(plain, bs, D))
