@@ -226,10 +226,10 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  * k (the sample misjudged it) is recomputed in full by its select workgroup
  * (its logits into its workspace segment, then an exact radix select), so the
  * output is exact for every input; such rows only take longer.
- * Supported: every head count, block size and kv_layout that
- * paged_mqa_logits_decode takes at head_dim 128 (head_dim 64 ->
- * MQA_ERR_UNSUPPORTED); the ring_depth tunable 0 or the logits
- * call's default (3 for 64-token blocks at 32 heads, else 4); a KV split of
+ * Supported: every head count, head dim, block size and kv_layout that
+ * paged_mqa_logits_decode takes; the ring_depth tunable 0 or the logits
+ * call's default (3 for 64-token blocks at 32 heads and head dim 128, else
+ * 4); a KV split of
  * at most 1024.  Errors as for paged_mqa_logits_decode (a shape outside its
  * gate -> MQA_ERR_UNSUPPORTED, checked first), plus: k out of range, another
  * ring_depth, NULL or misaligned indices or workspace, a workspace smaller

@@ -25,7 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmqa_indexer.so")
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "decode_heads.hip", "decode_d64.hip",
-           "decode_fused.hip", "topk.hip", "kcache.hip"]
+           "decode_fused.hip", "decode_fused_d64.hip", "topk.hip", "kcache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

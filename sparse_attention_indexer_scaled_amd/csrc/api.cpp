@@ -363,14 +363,13 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
 {
     if (k < 1 || k > mqa::kMaxTopK)
         return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
-    if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0 ||
-        head_dim != 128)
+    if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "the fused top-k takes the decode's shapes at head_dim 128: num_heads 32, 64 "
-                    "or 128, kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)", num_heads,
-                    head_dim, kv_block_size);
+                    "the fused top-k takes the decode's shapes: num_heads 32, 64 or 128, head_dim "
+                    "128 with kv_block_size 1, 16, 64 or 128, or head_dim 64 with kv_block_size "
+                    "16, 64 or 128 (got %d, %d, %d)", num_heads, head_dim, kv_block_size);
     // the sample and filter modes are built for the logits call's default ring
-    const int depth = (kv_block_size == 64 && num_heads == 32) ? 3 : 4;
+    const int depth = (kv_block_size == 64 && num_heads == 32 && head_dim == 128) ? 3 : 4;
     if (tun && tun->ring_depth != 0 && tun->ring_depth != depth)
         return fail(MQA_ERR_INVALID_ARG, "the fused top-k runs the default ring depth (0 or %d "
                     "for this shape)", depth);
@@ -402,7 +401,7 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
     mqa::FusedTopkLaunch f{&w,      context_lens, indices, batch,   next_n,
                            max_model_len, k,   p.split_kv, q_fp8, kv_cache,
                            weights, block_tables, max_blocks_per_seq, p.tiled,
-                           kv_block_size, p.head_tiles};
+                           kv_block_size, p.head_tiles, head_dim};
     hipError_t e;
     // 1. the sample: kFusedSampleChunks runs of steps per sequence
     mqa::DecodeLaunch ps = p;

@@ -2,8 +2,8 @@
 // The kernel template, its work decomposition and its gather are in
 // decode_kernel.h; 64 and 128 heads are launched from decode_heads.hip, head
 // dim 64 from decode_d64.hip, the fused top-k's sample and filter modes from
-// decode_fused.hip (separate translation units, so the instantiations compile
-// in parallel).
+// decode_fused.hip and decode_fused_d64.hip (separate translation units, so
+// the instantiations compile in parallel).
 #include "decode_kernel.h"
 
 namespace mqa {
@@ -13,7 +13,7 @@ int decode_ring_bytes(int depth) { return depth * kSlotBytes; }
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream)
 {
     if (p.mode != kLogits)
-        return launch_decode_fused(p, stream);
+        return p.head_dim == 64 ? launch_decode_fused_d64(p, stream) : launch_decode_fused(p, stream);
     if (p.head_dim == 64)
         return launch_decode_d64(p, stream);
     if (p.head_tiles != 1)

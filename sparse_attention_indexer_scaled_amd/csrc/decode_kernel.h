@@ -404,8 +404,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
 
     if (st0 < st1) {
         constexpr int H = kHeads * HT;
-        static_assert(DIM == kDim || (BS != 1 && MODE == kLogits),
-                      "head dim 64: blocks of 16 or more tokens, logits only");
+        static_assert(DIM == kDim || BS != 1, "head dim 64: blocks of 16 or more tokens");
         Operand<DIM> q[R][HT];
         Weights16 w[R][HT];
         // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f)

@@ -44,7 +44,7 @@ struct DecodeLaunch {
                    // 4 for block sizes other than 64
     int block_size;  // tokens per cache block: 1, 16, 64 or 128
     int head_tiles;  // num_heads / 32: 1, 2 or 4 (2 and 4: depth 4)
-    int head_dim;    // 128, or 64 (blocks of 16 or more tokens, depth 4, logits only)
+    int head_dim;    // 128, or 64 (blocks of 16 or more tokens, depth 4)
     int tiled;       // 1: K rows in the preshuffled (16,16) order (block size >= 16)
     // fused top-k only (zero / NULL for the logits call):
     int mode;              // 0 logits, 1 sample, 2 filter (modes 1, 2: the default depth,
@@ -127,6 +127,7 @@ struct FusedTopkLaunch {
     int tiled;
     int block_size;  // 1, 16, 64 or 128
     int head_tiles;  // num_heads / 32: 1, 2 or 4
+    int head_dim;    // 128 or 64
 };
 
 struct KcacheLaunch {
@@ -149,6 +150,7 @@ hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
 hipError_t launch_decode_heads(const DecodeLaunch &p, hipStream_t stream);  // 64, 128 heads
 hipError_t launch_decode_d64(const DecodeLaunch &p, hipStream_t stream);    // head dim 64
 hipError_t launch_decode_fused(const DecodeLaunch &p, hipStream_t stream);  // modes 1 and 2
+hipError_t launch_decode_fused_d64(const DecodeLaunch &p, hipStream_t stream);  // at head dim 64
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream);
 hipError_t launch_fused_threshold(const FusedTopkLaunch &p, hipStream_t stream);
 hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream);

@@ -919,8 +919,9 @@ __global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
 // 32 HT heads per wave, K straight from the cache), so every value equals the
 // decode call's.  Each lane finds its token's block through the table, for
 // any block size; entries past the last one holding a window token are never
-// read (a later token reuses it, and its value is never kept).
-template <int HT>
+// read (a later token reuses it, and its value is never kept).  DIM is the
+// head dim (128 or 64).
+template <int HT, int DIM>
 __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, int r, int tid,
                                               int lane, int wave)
 {
@@ -932,15 +933,15 @@ __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, 
     const int bound = ctx - ra.next_n + j;  // inclusive
     const int t = lane & 31, g = lane >> 5;
     const int bs = ra.block_size;
-    const int64_t blk_bytes = (int64_t)bs * (kDim + 4);
+    const int64_t blk_bytes = (int64_t)bs * (DIM + 4);
     const int last = max(nvalid - 1, 0) / bs;
     // With 16 waves a workgroup has 128 VGPRs per lane, so at most one head
     // tile's Q and weights stay in registers: 32 heads keep theirs for the
     // whole row, more heads reload them per step, tile by tile, summed in the
     // decode kernel's order.
-    const uint8_t *qrow = ra.q + (int64_t)r * (H * kDim) + t * kDim;
+    const uint8_t *qrow = ra.q + (int64_t)r * (H * DIM) + t * DIM;
     const float *wrow = ra.weights + (int64_t)r * H;
-    Frag q0;
+    Operand<DIM> q0;
     Weights16 w0;
     if constexpr (HT == 1) {
         load_frag(q0, qrow, lane);
@@ -949,17 +950,17 @@ __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, 
     const int32_t *table = ra.tables + (int64_t)b * ra.mbps;
     const float ninf = -__builtin_inff();
     for (int st = wave; st < nsteps; st += kWaves) {
-        KStep k;
+        KStepOf<DIM> k;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int p = st * kStep + kTile * h + t;
             const int slot = p % bs;
             const uint8_t *blk = ra.cache + (int64_t)table[min(p / bs, last)] * blk_bytes;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < DIM / 32; ++c) {
                 const int u = 2 * c + g;  // 16-byte granule of the row
-                const int off = ra.tiled ? (slot >> 4) * (16 * kDim) + u * 256 + (slot & 15) * 16
-                                         : slot * kDim + u * 16;
+                const int off = ra.tiled ? (slot >> 4) * (16 * DIM) + u * 256 + (slot & 15) * 16
+                                         : slot * DIM + u * 16;
                 if (bs == 1) {
                     // per-token records are 132 bytes: K rows only 4-byte aligned
                     const int *src = reinterpret_cast<const int *>(blk + off);
@@ -968,7 +969,7 @@ __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, 
                     k.t[h].c[c] = *reinterpret_cast<const i32x4 *>(blk + off);
                 }
             }
-            k.sc[h] = *reinterpret_cast<const float *>(blk + bs * kDim + 4 * slot);
+            k.sc[h] = *reinterpret_cast<const float *>(blk + bs * DIM + 4 * slot);
         }
         float part[2];
         if constexpr (HT == 1) {
@@ -978,9 +979,9 @@ __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, 
         } else {
 #pragma unroll 1
             for (int ht = 0; ht < HT; ++ht) {
-                Frag q;
+                Operand<DIM> q;
                 Weights16 w;
-                load_frag(q, qrow + ht * (kHeads * kDim), lane);
+                load_frag(q, qrow + ht * (kHeads * DIM), lane);
                 load_weights(w, wrow + ht * kHeads, lane);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -1006,7 +1007,7 @@ __device__ __forceinline__ void recompute_row(float *x, const FusedRowArgs &ra, 
         x[p] = ninf;
 }
 
-template <int HT>
+template <int HT, int DIM>
 __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
                                                                 const int *__restrict__ counts,
                                                                 int split, int k,
@@ -1060,7 +1061,7 @@ __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
     } else {
         // the row's own segment region (>= mml floats) now holds its logits
         float *x = reinterpret_cast<float *>(row);
-        recompute_row<HT>(x, ra, r, tid, lane, wave);
+        recompute_row<HT, DIM>(x, ra, r, tid, lane, wave);
         __threadfence_block();
         __syncthreads();
         n = radix_select(sh, x, ra.mml, k, tid, lane, wave);
@@ -1069,16 +1070,16 @@ __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
     sort_and_write(sh, n, out, k, tid, lane, wave);
 }
 
-template <int HT>
+template <int HT, int DIM>
 hipError_t launch_fused_select_ht(const FusedTopkLaunch &p, const FusedRowArgs &ra,
                                   hipStream_t stream)
 {
     static std::atomic<uint64_t> raised{0};
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&fused_select_kernel<HT>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&fused_select_kernel<HT, DIM>),
                                    (int)sizeof(TopkShared), raised);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(fused_select_kernel<HT>, dim3(p.batch * p.next_n), dim3(kThreads),
+    hipLaunchKernelGGL((fused_select_kernel<HT, DIM>), dim3(p.batch * p.next_n), dim3(kThreads),
                        sizeof(TopkShared), stream, ra, p.ws->counts, p.split, p.k, p.indices,
                        p.ws->recomputed);
     return hipGetLastError();
@@ -1108,10 +1109,13 @@ hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream)
     ra.mbps = p.max_blocks_per_seq;
     ra.tiled = p.tiled;
     ra.block_size = p.block_size;
-    switch (p.head_tiles) {
-    case 1: return launch_fused_select_ht<1>(p, ra, stream);
-    case 2: return launch_fused_select_ht<2>(p, ra, stream);
-    case 4: return launch_fused_select_ht<4>(p, ra, stream);
+    switch (p.head_tiles * 1000 + p.head_dim) {
+    case 1128: return launch_fused_select_ht<1, 128>(p, ra, stream);
+    case 2128: return launch_fused_select_ht<2, 128>(p, ra, stream);
+    case 4128: return launch_fused_select_ht<4, 128>(p, ra, stream);
+    case 1064: return launch_fused_select_ht<1, 64>(p, ra, stream);
+    case 2064: return launch_fused_select_ht<2, 64>(p, ra, stream);
+    case 4064: return launch_fused_select_ht<4, 64>(p, ra, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -191,7 +191,12 @@ def test_fused_topk_validation(lib):
     # the shapes the decode takes, checked before any pointer
     assert _fused(lib, nulls, H=48) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, bs=32) == E.MQA_ERR_UNSUPPORTED
-    assert _fused(lib, nulls, D=64) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, D=96) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, D=64, bs=1) == E.MQA_ERR_UNSUPPORTED
+    assert _fused(lib, nulls, D=64) == E.MQA_ERR_INVALID_ARG  # head dim 64: supported; NULLs
+    assert _fused(lib, nulls, D=64, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
+        E.MQA_ERR_INVALID_ARG
+    assert "ring depth" in mqa.last_error()
     for H, bs in ((64, 64), (128, 64), (32, 16), (32, 1), (32, 128), (64, 16), (128, 1)):
         assert _fused(lib, nulls, H=H, bs=bs) == E.MQA_ERR_INVALID_ARG
         assert "NULL" in mqa.last_error()

@@ -106,15 +106,15 @@ def _preshuffle(d, preshuffle):
     return d
 
 
-def _integer_decode(B, next_n, ctx, mml, seed, H=32, bs=64, preshuffle=False):
+def _integer_decode(B, next_n, ctx, mml, seed, H=32, bs=64, preshuffle=False, D=128):
     """Integer fp8 values in [-8, 8] and power-of-two weights and scales:
     every logit is exact in fp32, whatever the accumulation order."""
     rng = np.random.default_rng(seed)
-    d = inputs.make_decode(B, next_n, ctx, mml, seed=seed, H=H, block_size=bs, poison=True)
+    d = inputs.make_decode(B, next_n, ctx, mml, seed=seed, H=H, D=D, block_size=bs, poison=True)
     d.q = inputs.to_fp8_bytes(rng.integers(-8, 9, d.q.shape).astype(np.float32))
     d.weights = (rng.choice([-1, 1], d.weights.shape) *
                  2.0 ** -rng.integers(0, 4, d.weights.shape)).astype(np.float32)
-    kview, sview = inputs.cache_views(d.kv_cache, bs, 128)
+    kview, sview = inputs.cache_views(d.kv_cache, bs, D)
     used = d.num_blocks - 1  # the last block is the poison block
     kview[:used] = inputs.to_fp8_bytes(rng.integers(-8, 9, kview[:used].shape).astype(np.float32))
     sview[:used] = rng.choice([0.5, 1.0, 2.0], sview[:used].shape).astype(np.float32)
@@ -148,7 +148,7 @@ def _one_hot_logits(d, high_positions):
     d.q[:] = 0
     d.q[..., 0] = 0x38  # 1.0
     d.weights[:] = np.float32(1.0 / d.H)
-    kview, sview = inputs.cache_views(d.kv_cache, bs, 128)
+    kview, sview = inputs.cache_views(d.kv_cache, bs, d.D)
     used = d.num_blocks - 1
     kview[:used] = 0
     sview[:used] = 1.0
@@ -178,18 +178,19 @@ def test_fused_rows_the_sample_misjudges():
             assert np.array_equal(got[1], np.arange(2048))
 
 
-# Every other cache layout and head count the logits call takes:
-# (kv_block_size, num_heads, preshuffled)
-LAYOUTS = [(16, 32, False), (16, 32, True), (128, 32, False), (128, 32, True), (1, 32, False),
-           (64, 64, False), (64, 128, True)]
-LAYOUT_IDS = ["bs%d-h%d%s" % (bs, h, "-pre" if pre else "") for bs, h, pre in LAYOUTS]
+# Every other cache layout, head count and head dim the logits call takes:
+# (kv_block_size, num_heads, preshuffled, head_dim)
+LAYOUTS = [(16, 32, False, 128), (16, 32, True, 128), (128, 32, False, 128), (128, 32, True, 128),
+           (1, 32, False, 128), (64, 64, False, 128), (64, 128, True, 128), (64, 32, False, 64),
+           (16, 64, True, 64), (128, 128, False, 64)]
+LAYOUT_IDS = ["bs%d-h%d-d%d%s" % (bs, h, dd, "-pre" if pre else "") for bs, h, pre, dd in LAYOUTS]
 
 
-@pytest.mark.parametrize("bs,H,pre", LAYOUTS, ids=LAYOUT_IDS)
-def test_fused_other_layouts_equal_topk_of_logits(bs, H, pre):
+@pytest.mark.parametrize("bs,H,pre,D", LAYOUTS, ids=LAYOUT_IDS)
+def test_fused_other_layouts_equal_topk_of_logits(bs, H, pre, D):
     """Short rows (keep-all), the sampled threshold on long rows, an empty and
-    a tiny sequence, in every block size, K order and head count."""
-    d = inputs.make_decode(4, 3, [20000, 0, 9000, 5], 20032, seed=940 + bs + H, H=H,
+    a tiny sequence, in every block size, K order, head count and head dim."""
+    d = inputs.make_decode(4, 3, [20000, 0, 9000, 5], 20032, seed=940 + bs + H, H=H, D=D,
                            block_size=bs, preshuffle=pre, poison=True)
     dv = decode_device_inputs(d)
     for k in (64, 2048):
@@ -197,22 +198,23 @@ def test_fused_other_layouts_equal_topk_of_logits(bs, H, pre):
         assert_same(fused(d, k, dv=dv), unfused(d, k, dv=dv), "bs=%d H=%d k=%d" % (bs, H, k))
 
 
-@pytest.mark.parametrize("bs,H,pre", LAYOUTS, ids=LAYOUT_IDS)
-def test_fused_other_layouts_integer_inputs_match_the_oracle(bs, H, pre):
-    d = _integer_decode(2, 2, [12000, 700], 12032, seed=950 + bs + H, H=H, bs=bs, preshuffle=pre)
+@pytest.mark.parametrize("bs,H,pre,D", LAYOUTS, ids=LAYOUT_IDS)
+def test_fused_other_layouts_integer_inputs_match_the_oracle(bs, H, pre, D):
+    d = _integer_decode(2, 2, [12000, 700], 12032, seed=950 + bs + H, H=H, bs=bs, preshuffle=pre,
+                        D=D)
     ref = oracle.decode(d.q, d.kv_cache, d.weights, d.context_lens, d.block_tables,
                         d.max_model_len, bs, preshuffle=pre).astype(np.float32)
     say("fused topk integer inputs bs=%d H=%d preshuffle=%s" % (bs, H, pre))
     assert_same(fused(d, 2048), oracle_topk(ref, 2048), "integer bs=%d H=%d" % (bs, H))
 
 
-@pytest.mark.parametrize("bs,H,pre", LAYOUTS, ids=LAYOUT_IDS)
-def test_fused_other_layouts_rows_the_sample_misjudges(bs, H, pre):
+@pytest.mark.parametrize("bs,H,pre,D", LAYOUTS, ids=LAYOUT_IDS)
+def test_fused_other_layouts_rows_the_sample_misjudges(bs, H, pre, D):
     """The full-row recompute of the select kernel in every layout: row 0 has
     its 1000 logits of 1 inside the sample (too few kept for k = 2048), row 1
     is constant (too many kept)."""
     ctx = 16384
-    d = inputs.make_decode(2, 1, [ctx, ctx], ctx, seed=960 + bs + H, H=H, block_size=bs,
+    d = inputs.make_decode(2, 1, [ctx, ctx], ctx, seed=960 + bs + H, H=H, D=D, block_size=bs,
                            poison=True)
     sampled = np.concatenate([np.arange(64 * s, 64 * s + 64) for s in _sampled_steps(ctx // 64)])
     high = np.sort(np.random.default_rng(961).choice(sampled, 1000, replace=False))
