@@ -83,10 +83,9 @@ typedef struct mqa_tunables {
  * num_heads 32, 64 or 128 (the head counts the issue page about next_n tiling
  * sweeps) with head_dim 128 or 64 (the head dims of the aiter PR 5046 page's
  * test sweep, "Test Plan").  kv_block_size: 0 asks about prefill; 1, 16, 64 or
- * 128 about paged decode with blocks of that many tokens (at every head
- * count; head_dim 64 needs blocks of 16 or more tokens).  Returns 1 if the
- * current HIP device is gfx950 and the shape is supported, else 0.  Never
- * fails.
+ * 128 about paged decode with blocks of that many tokens (at every head count
+ * and head dim).  Returns 1 if the current HIP device is gfx950 and the shape
+ * is supported, else 0.  Never fails.
  */
 int mqa_is_supported(int num_heads, int head_dim, int kv_block_size);
 
@@ -165,9 +164,9 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * Entries past that are never read.  Scales must be >= 0.  Cache slots past a
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
- * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads and head_dim 128;
- * head_dim 64 with kv_block_size 16, 64 or 128 (a block of bs tokens is then
- * bs * 68 bytes).  The ring_depth tunable may differ from 4 only with
+ * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads and head_dim 128 or
+ * 64 (a block of bs tokens is then bs * 68 bytes).  The ring_depth tunable may
+ * differ from 4 only with
  * kv_block_size 64, 32 heads and head_dim 128.  kv_layout MQA_KV_SLOT_MAJOR
  * or MQA_KV_PRESHUFFLED (the latter not with kv_block_size 1).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
@@ -272,8 +271,8 @@ size_t paged_mqa_topk_workspace_size(int batch, int next_n, int max_model_len);
  * num_tokens == 0 is a successful no-op.  Negative sizes, a bad k_dtype or
  * kv_layout, NULL or misaligned pointers (k and kv_cache 16-byte,
  * slot_mapping 8-byte) -> MQA_ERR_INVALID_ARG; head_dim other than 128 or 64,
- * kv_block_size not 1, 16, 64 or 128, head_dim 64 with kv_block_size 1, or the
- * preshuffled layout with kv_block_size 1 -> MQA_ERR_UNSUPPORTED.
+ * kv_block_size not 1, 16, 64 or 128, or the preshuffled layout with
+ * kv_block_size 1 -> MQA_ERR_UNSUPPORTED.
  */
 int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int64_t *slot_mapping,
                                uint8_t *kv_cache, int num_tokens, int head_dim,

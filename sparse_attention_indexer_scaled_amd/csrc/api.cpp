@@ -81,14 +81,13 @@ int check_device()
 
 // 32, 64 or 128 index heads (the pages sweep all three); head dim 128 or 64
 // (the prefill page's test sweep covers head dims 64 and 128, the decode
-// page's only 128; the decode takes 64 too, in blocks of 16 or more tokens);
-// cache blocks of 1, 16, 64 or 128 tokens for decode (0 asks about prefill),
-// at every head count.
+// page's only 128; the decode takes 64 too); cache blocks of 1, 16, 64 or 128
+// tokens for decode (0 asks about prefill), at every head count and head dim.
 bool shape_supported(int num_heads, int head_dim, int kv_block_size)
 {
     if (num_heads != 32 && num_heads != 64 && num_heads != 128)
         return false;
-    if (head_dim != 128 && !(head_dim == 64 && kv_block_size != 1))
+    if (head_dim != 128 && head_dim != 64)
         return false;
     return kv_block_size == 0 || kv_block_size == 1 || kv_block_size == 16 ||
            kv_block_size == 64 || kv_block_size == 128;
@@ -230,9 +229,8 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
                     "(got %d)", kv_layout);
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "decode supports num_heads 32, 64 or 128, head_dim 128 with kv_block_size "
-                    "1, 16, 64 or 128, or head_dim 64 with kv_block_size 16, 64 or 128 "
-                    "(got %d, %d, %d)",
+                    "decode supports num_heads 32, 64 or 128, head_dim 128 or 64 and "
+                    "kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)",
                     num_heads, head_dim, kv_block_size);
     if (kv_layout == MQA_KV_PRESHUFFLED && kv_block_size < 16)
         return fail(MQA_ERR_UNSUPPORTED, "the preshuffled layout needs kv_block_size 16, 64 or 128 "
@@ -366,8 +364,8 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
     if (!shape_supported(num_heads, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
                     "the fused top-k takes the decode's shapes: num_heads 32, 64 or 128, head_dim "
-                    "128 with kv_block_size 1, 16, 64 or 128, or head_dim 64 with kv_block_size "
-                    "16, 64 or 128 (got %d, %d, %d)", num_heads, head_dim, kv_block_size);
+                    "128 or 64, kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)", num_heads,
+                    head_dim, kv_block_size);
     // the sample and filter modes are built for the logits call's default ring
     const int depth = (kv_block_size == 64 && num_heads == 32 && head_dim == 128) ? 3 : 4;
     if (tun && tun->ring_depth != 0 && tun->ring_depth != depth)
@@ -472,8 +470,8 @@ extern "C" int mqa_kcache_quantize_insert(const void *k, int k_dtype, const int6
                     k_dtype);
     if (!shape_supported(32, head_dim, kv_block_size) || kv_block_size == 0)
         return fail(MQA_ERR_UNSUPPORTED,
-                    "K-cache insert supports head_dim 128 with kv_block_size 1, 16, 64 or 128, or "
-                    "head_dim 64 with kv_block_size 16, 64 or 128 "
+                    "K-cache insert supports head_dim 128 or 64 and kv_block_size 1, 16, 64 or "
+                    "128 "
                     "(got %d, %d)",
                     head_dim, kv_block_size);
     if (kv_layout != MQA_KV_SLOT_MAJOR && kv_layout != MQA_KV_PRESHUFFLED)

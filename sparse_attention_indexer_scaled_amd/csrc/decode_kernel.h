@@ -226,8 +226,10 @@ __device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_pe
 // 4-byte global->LDS loads: dword load jj of chunk c writes LDS bytes
 // 1024 c + 256 jj + 4 i from lane i, i.e. byte 4 (i % 4) of granule
 // position 16 jj + i / 4, which holds granule q = position ^ 8 (c & 1): token
-// 8c + (i / 4) % 8, 16-byte granule 2 jj + ((i / 32) ^ (c & 1)).  So each lane
-// needs one entry per chunk, and four loads move a chunk.
+// 8c + (i / 4) % 8, 16-byte granule 2 jj + ((i / 32) ^ (c & 1)).  At head dim
+// 64 (68-byte records, chunks of 16 unswizzled rows) the same byte holds
+// token 16c + i / 4, granule jj.  So each lane needs one entry per chunk, and
+// four loads move a chunk.
 constexpr int kTokLoadsPerChunk = 4;
 
 __device__ __forceinline__ int32_t lds_read_i32(uint32_t addr)
@@ -237,11 +239,11 @@ __device__ __forceinline__ int32_t lds_read_i32(uint32_t addr)
     return v;
 }
 
-template <int G>
+template <int G, int DIM = kDim>
 __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, const uint8_t *cache,
                                                int g, int lane)
 {
-    constexpr int KC = kChunks - 1;
+    constexpr int KC = k_chunks<DIM>();
     constexpr int J = (KC + G - 1) / G;
     const bool scales = G == 1 || g == G - 1;
     int32_t ent[J];
@@ -251,7 +253,8 @@ __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, c
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int c = g + G * j;
-        ent[j] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * (8 * c + ((lane >> 2) & 7))) : 0;
+        const int tok = DIM == 128 ? 8 * c + ((lane >> 2) & 7) : 16 * c + (lane >> 2);
+        ent[j] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * tok) : 0;
     }
     if (scales)
         ent_s = lds_read_i32(entries + 4 * lane);
@@ -261,18 +264,18 @@ __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, c
         asm volatile("" : "+v"(ent[j]));
         const int c = g + G * j;
         if (G * J == KC || c < KC) {
-            const uint8_t *src = cache + (int64_t)ent[j] * (kDim + 4) +
-                                 16 * (((lane >> 5) ^ (c & 1))) + 4 * (lane & 3);
+            const uint8_t *src = cache + (int64_t)ent[j] * (DIM + 4) +
+                                 (DIM == 128 ? 16 * ((lane >> 5) ^ (c & 1)) : 0) + 4 * (lane & 3);
 #pragma unroll
             for (int jj = 0; jj < kTokLoadsPerChunk; ++jj)
-                __builtin_amdgcn_global_load_lds(src + 32 * jj, slot + 1024 * c + 256 * jj, 4, 0,
-                                                 kStreamHint);
+                __builtin_amdgcn_global_load_lds(src + (DIM == 128 ? 32 : 16) * jj,
+                                                 slot + 1024 * c + 256 * jj, 4, 0, kStreamHint);
         }
     }
     if (scales) {
         asm volatile("" : "+v"(ent_s));
-        __builtin_amdgcn_global_load_lds(cache + (int64_t)ent_s * (kDim + 4) + kDim,
-                                         slot + kBlock * kDim, 4, 0, kStreamHint);
+        __builtin_amdgcn_global_load_lds(cache + (int64_t)ent_s * (DIM + 4) + DIM,
+                                         slot + kStep * DIM, 4, 0, kStreamHint);
     }
 }
 
@@ -404,7 +407,6 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
 
     if (st0 < st1) {
         constexpr int H = kHeads * HT;
-        static_assert(DIM == kDim || BS != 1, "head dim 64: blocks of 16 or more tokens");
         Operand<DIM> q[R][HT];
         Weights16 w[R][HT];
         // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f)
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
 #pragma unroll
             for (int i = 0; i < D - 1; ++i)
                 if (st0 + i < st1)
-                    request_tokens<G>(ring + i * SB, tring_addr + i * (kStep * 4), cache, g,
+                    request_tokens<G, DIM>(ring + i * SB, tring_addr + i * (kStep * 4), cache, g,
                                       lane);
         } else {
 #pragma unroll
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                 if (g == 0 && st + kTabSlots < st1)
                     request_table(st + kTabSlots);
                 if (st + D - 1 < st1)
-                    request_tokens<G>(ring + wr * SB,
+                    request_tokens<G, DIM>(ring + wr * SB,
                                       tring_addr + ((st + D - 1 - st0) % kTabSlots) * (kStep * 4),
                                       cache, g, lane);
             } else {
@@ -642,9 +644,8 @@ hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hip
 // The kernels a (rows per wave R, waves G, head tiles HT, mode, head dim)
 // launch can take, by block size and ring depth: 64-token blocks at 32 heads
 // and head dim 128 take ring depths 2..7 for the logits call and 3 for the
-// fused top-k's modes; every other layout takes depth 4, and head dim 64
-// blocks of 16 or more tokens.  (Q and weights of a wave's rows stay in
-// VGPRs, so R HT <= 4.)
+// fused top-k's modes; every other layout takes depth 4.  (Q and weights of
+// a wave's rows stay in VGPRs, so R HT <= 4.)
 template <int R, int G, int HT, int MODE, int DIM = kDim>
 hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
@@ -672,11 +673,7 @@ hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipSt
         if (p.depth != 4)
             return hipErrorInvalidValue;
         switch (p.block_size) {
-        case 1:
-            if constexpr (DIM == kDim)
-                return launch_rgdb<R, G, 4, 1, HT, MODE>(p, a, grid, stream);
-            else
-                return hipErrorInvalidValue;
+        case 1: return launch_rgdb<R, G, 4, 1, HT, MODE, DIM>(p, a, grid, stream);
         case 16: return launch_rgdb<R, G, 4, 16, HT, MODE, DIM>(p, a, grid, stream);
         case 64:
             if constexpr (HT > 1 || DIM != kDim)

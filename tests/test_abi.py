@@ -122,8 +122,7 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls, bs=0) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, H=48) == mqa._native.MQA_ERR_UNSUPPORTED
     assert _decode(lib, nulls, D=96) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert _decode(lib, nulls, D=64, bs=1) == mqa._native.MQA_ERR_UNSUPPORTED
-    for bs in (16, 64, 128):  # head dim 64: blocks of 16 or more tokens
+    for bs in (1, 16, 64, 128):  # head dim 64: every block size
         assert _decode(lib, nulls, D=64, bs=bs) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
         assert "NULL" in mqa.last_error()
     bad = _native.Tunables(ring_depth=3)  # head dim 64: ring depth 0 or 4
@@ -192,8 +191,8 @@ def test_fused_topk_validation(lib):
     assert _fused(lib, nulls, H=48) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, bs=32) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, D=96) == E.MQA_ERR_UNSUPPORTED
-    assert _fused(lib, nulls, D=64, bs=1) == E.MQA_ERR_UNSUPPORTED
-    assert _fused(lib, nulls, D=64) == E.MQA_ERR_INVALID_ARG  # head dim 64: supported; NULLs
+    assert _fused(lib, nulls, D=64, bs=1) == E.MQA_ERR_INVALID_ARG  # head dim 64: NULLs
+    assert _fused(lib, nulls, D=64) == E.MQA_ERR_INVALID_ARG
     assert _fused(lib, nulls, D=64, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
         E.MQA_ERR_INVALID_ARG
     assert "ring depth" in mqa.last_error()
@@ -227,7 +226,8 @@ def test_kcache_validation(lib):
     assert f(None, 2, None, None, 5, 128, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG
     assert "k_dtype" in mqa.last_error()
     assert f(None, 0, None, None, 5, 96, 64, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
-    assert f(None, 0, None, None, 5, 64, 1, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
+    assert f(None, 0, None, None, 5, 64, 1, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
+    assert f(None, 0, None, None, 5, 64, 1, 1, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
     assert f(None, 0, None, None, 5, 64, 64, 0, 4, None) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
     assert f(None, 1, None, None, 5, 128, 32, 0, 4, None) == mqa._native.MQA_ERR_UNSUPPORTED
     assert f(None, 0, None, None, 5, 128, 64, 3, 4, None) == mqa._native.MQA_ERR_INVALID_ARG

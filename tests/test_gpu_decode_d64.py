@@ -1,6 +1,6 @@
 """GPU parity of the paged decode at head dim 64 (64-byte K rows, one fp8
-MFMA per row, tile and head tile): 32, 64 and 128 heads, blocks of 16, 64 and
-128 tokens, slot-major and preshuffled K.
+MFMA per row, tile and head tile): 32, 64 and 128 heads, blocks of 1, 16, 64
+and 128 tokens, slot-major and (blocks of 16 or more) preshuffled K.
 
 An exact integer pin (bit for bit against the oracle), random inputs element by
 element against the oracle, and bitwise invariance under launch tunables,
@@ -24,7 +24,7 @@ D = 64
 def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     lib()
-    assert is_supported(32, D, 64) and is_supported(128, D, 16) and not is_supported(32, D, 1)
+    assert is_supported(32, D, 64) and is_supported(128, D, 16) and is_supported(32, D, 1)
 
 
 def _integer(d, rng):
@@ -41,8 +41,8 @@ def _integer(d, rng):
 
 
 @pytest.mark.parametrize("H", [32, 64, 128])
-@pytest.mark.parametrize("bs", [16, 64, 128])
-@pytest.mark.parametrize("pre", [False, True], ids=["slot-major", "preshuffled"])
+@pytest.mark.parametrize("bs,pre", [(1, False), (16, False), (64, False), (128, False), (16, True),
+                                    (64, True), (128, True)])
 def test_integer_inputs_bit_exact(H, bs, pre):
     rng = np.random.default_rng(800 + H + bs)
     d = inputs.make_decode(3, 3, [700, 64, 131], 800, seed=800 + bs, H=H, D=D, block_size=bs,
@@ -69,7 +69,7 @@ def test_integer_inputs_bit_exact_every_row_split(next_n):
 
 
 @pytest.mark.parametrize("H", [32, 64, 128])
-@pytest.mark.parametrize("bs", [16, 64, 128])
+@pytest.mark.parametrize("bs", [1, 16, 64, 128])
 @pytest.mark.parametrize("B,next_n,ctx,mml", [(3, 2, [700, 130, 3000], 3072),
                                               (4, 1, [0, 15, 65, 4100], 4160),
                                               (2, 6, [2000, 7], 2001)])
@@ -91,8 +91,8 @@ def test_tunables_block_sizes_and_k_order_do_not_change_bits(H):
     kw = dict(B=3, next_n=6, context_lens=[2000, 150, 1300], max_model_len=2048, seed=860 + H,
               H=H, D=D)
     base = run_decode(inputs.make_decode(block_size=64, **kw))
-    for bs in (16, 64, 128):
-        for pre in (False, True):
+    for bs in (1, 16, 64, 128):
+        for pre in ((False,) if bs == 1 else (False, True)):
             d = inputs.make_decode(block_size=bs, preshuffle=pre, **kw)
             say("decode d64 H=%d bs=%d preshuffle=%s vs 64-token slot-major" % (H, bs, pre))
             assert np.array_equal(run_decode(d), base, equal_nan=True)

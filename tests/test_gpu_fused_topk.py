@@ -182,7 +182,7 @@ def test_fused_rows_the_sample_misjudges():
 # (kv_block_size, num_heads, preshuffled, head_dim)
 LAYOUTS = [(16, 32, False, 128), (16, 32, True, 128), (128, 32, False, 128), (128, 32, True, 128),
            (1, 32, False, 128), (64, 64, False, 128), (64, 128, True, 128), (64, 32, False, 64),
-           (16, 64, True, 64), (128, 128, False, 64)]
+           (16, 64, True, 64), (128, 128, False, 64), (1, 64, False, 64)]
 LAYOUT_IDS = ["bs%d-h%d-d%d%s" % (bs, h, dd, "-pre" if pre else "") for bs, h, pre, dd in LAYOUTS]
 
 

@@ -27,8 +27,8 @@ def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     lib()
     assert all(is_supported(h, D, 0) for h in HEADS)
-    # the decode takes head dim 64 in blocks of 16 or more tokens, not per-token blocks
-    assert is_supported(32, D, 64) and not is_supported(32, D, 1)
+    # the decode takes head dim 64 in every block size
+    assert is_supported(32, D, 64) and is_supported(32, D, 1)
 
 
 def _block_ms(H):

@@ -140,8 +140,8 @@ def test_zero_tokens_is_a_no_op():
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("bs,pre", [(16, False), (64, False), (128, False), (16, True),
-                                    (64, True), (128, True)])
+@pytest.mark.parametrize("bs,pre", [(1, False), (16, False), (64, False), (128, False),
+                                    (16, True), (64, True), (128, True)])
 def test_insert_head_dim_64(bs, pre, bf16):
     """Head dim 64: 64 code bytes per token (one per lane), the scale after the
     block's 64-byte rows; the whole cache equals the oracle's bit for bit."""

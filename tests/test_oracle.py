@@ -164,6 +164,7 @@ def test_prefill_matches_exact_brute_force(H, D, M, N, mode):
     (2, 4, 2, 2, 4, [5, 9]),
     (32, 128, 1, 3, 64, [70]),
     (2, 64, 2, 2, 16, [20, 33]),
+    (2, 64, 2, 1, 1, [9, 4]),
     (3, 8, 3, 3, 2, [0, 2, 7]),
     (1, 1, 2, 1, 8, [17, 3]),
 ])
