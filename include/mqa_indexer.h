@@ -165,8 +165,9 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
  * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads and head_dim 128 or
- * 64 (a block of bs tokens is then bs * 68 bytes).  The ring_depth tunable may
- * differ from 4 only with
+ * 64 (a block of bs tokens is then bs * 68 bytes).  The ring_depth tunable
+ * takes 0 or the layout's one depth (4 for kv_block_size 1, else 3), except
+ * with
  * kv_block_size 64, 32 heads and head_dim 128.  kv_layout MQA_KV_SLOT_MAJOR
  * or MQA_KV_PRESHUFFLED (the latter not with kv_block_size 1).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
@@ -227,8 +228,7 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
  * output is exact for every input; such rows only take longer.
  * Supported: every head count, head dim, block size and kv_layout that
  * paged_mqa_logits_decode takes; the ring_depth tunable 0 or the logits
- * call's default (3 for 64-token blocks at 32 heads and head dim 128, else
- * 4); a KV split of
+ * call's default (4 for kv_block_size 1, else 3); a KV split of
  * at most 1024.  Errors as for paged_mqa_logits_decode (a shape outside its
  * gate -> MQA_ERR_UNSUPPORTED, checked first), plus: k out of range, another
  * ring_depth, NULL or misaligned indices or workspace, a workspace smaller

@@ -241,13 +241,15 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     const int head_tiles = num_heads / 32;
     const int max_rows = 4 / head_tiles;  // Q and weights of a wave's rows stay in VGPRs
     const bool any_depth = kv_block_size == 64 && head_tiles == 1 && head_dim == 128;
+    // the one ring depth the other layouts instantiate (see the heuristic)
+    const int fixed_depth = kv_block_size == 1 ? 4 : 3;
     if (t.rows_per_block < 0 || t.rows_per_block > max_rows || t.split_kv < 0 ||
         t.num_warps != 0 || t.ring_depth < 0 || t.ring_depth == 1 || t.ring_depth > 7 ||
-        (!any_depth && t.ring_depth != 0 && t.ring_depth != 4))
+        (!any_depth && t.ring_depth != 0 && t.ring_depth != fixed_depth))
         return fail(MQA_ERR_INVALID_ARG,
                     "decode tunables: rows_per_block in 0..%d, split_kv >= 0, ring_depth 0 or 2..7 "
-                    "(0 or 4 unless 32 heads, head_dim 128 and kv_block_size 64), num_warps 0",
-                    max_rows);
+                    "(0 or %d unless 32 heads, head_dim 128 and kv_block_size 64), num_warps 0",
+                    max_rows, fixed_depth);
     if (batch == 0 || max_model_len == 0)
         return kNoop;
     if (!q_fp8 || !kv_cache || !weights || !context_lens || !block_tables ||
@@ -283,9 +285,11 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     //         68.5 against 69.7 us, next_n 4 as 4 x 1 row 144.6 against
     //         146.7 us (ragged batch), each the mean of three alternating runs.
     //         Below that, ceil(next_n / 2) rows per wave.
-    //   depth: 3 steps (25 KiB) per workgroup for 64-token blocks and 32
-    //          heads (the other layouts instantiate 4 only); deeper rings cost
-    //          workgroups per CU and measured slower.
+    //   depth: 3 steps (25 KiB) per workgroup; deeper rings cost workgroups
+    //          per CU and measured slower.  The other layouts instantiate one
+    //          depth: 3 (16-token blocks 68.5 against 69-73 us at depth 4,
+    //          128-token blocks 69.9 against 70-73 us, the rest level) and 4
+    //          for per-token blocks (level).
     //   split: at least ~1024 workgroups, and at most 32 steps (2048 tokens)
     //          per workgroup at the longest context, but at least 2 steps;
     //          more workgroups per sequence than that measured slower (longer
@@ -300,7 +304,7 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     //   2-step ring (B 16, 8192 tokens: 6.6 -> 6.2 us).
     const int64_t steps_max = ceil_div(max_model_len, 64);
     const bool short_ctx = steps_max <= 128;
-    p.depth = t.ring_depth ? t.ring_depth : (any_depth ? (short_ctx ? 2 : 3) : 4);
+    p.depth = t.ring_depth ? t.ring_depth : (any_depth ? (short_ctx ? 2 : 3) : fixed_depth);
     p.block_size = kv_block_size;
     p.tiled = kv_layout == MQA_KV_PRESHUFFLED;
     if (t.split_kv) {
@@ -367,7 +371,7 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
                     "128 or 64, kv_block_size 1, 16, 64 or 128 (got %d, %d, %d)", num_heads,
                     head_dim, kv_block_size);
     // the sample and filter modes are built for the logits call's default ring
-    const int depth = (kv_block_size == 64 && num_heads == 32 && head_dim == 128) ? 3 : 4;
+    const int depth = kv_block_size == 1 ? 4 : 3;
     if (tun && tun->ring_depth != 0 && tun->ring_depth != depth)
         return fail(MQA_ERR_INVALID_ARG, "the fused top-k runs the default ring depth (0 or %d "
                     "for this shape)", depth);

@@ -1,7 +1,8 @@
 // Paged decode logits at head dim 64 (gfx950): 64-byte K rows, so a 64-token
 // step is four 1 KiB chunks of 16 rows, and one fp8 MFMA per (row, tile, head
 // tile) instead of two.  32, 64 and 128 heads; blocks of 16, 64 or 128 tokens
-// in either K order; ring depth 4 (kernel template in decode_kernel.h).
+// in either K order; ring depth 3, or 4 for per-token blocks (kernel
+// template in decode_kernel.h).
 #include "decode_kernel.h"
 
 namespace mqa {

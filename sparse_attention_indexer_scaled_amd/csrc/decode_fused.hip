@@ -1,7 +1,7 @@
 // The fused decode top-k's two decode modes (gfx950): the sample and the
 // filter (decode_kernel.h, DecodeMode), for every cache layout and head count
 // the logits call takes.  The ring depth is the logits call's default: 3
-// steps for 64-token blocks at 32 heads, 4 for the rest.
+// steps, 4 for per-token blocks.
 #include "decode_kernel.h"
 
 namespace mqa {

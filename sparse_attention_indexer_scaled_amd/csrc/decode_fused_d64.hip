@@ -1,5 +1,5 @@
 // The fused decode top-k's sample and filter modes at head dim 64 (gfx950):
-// 32, 64 and 128 heads, blocks of 16, 64 or 128 tokens, ring depth 4
+// 32, 64 and 128 heads, blocks of 1, 16, 64 or 128 tokens, the logits call's ring depth
 // (kernel template in decode_kernel.h).
 #include "decode_kernel.h"
 

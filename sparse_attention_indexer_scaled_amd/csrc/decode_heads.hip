@@ -1,6 +1,6 @@
 // Paged decode logits at 64 and 128 index heads (gfx950): 2 or 4 MFMA head
 // tiles per row over the same K stream, every block size and K order, ring
-// depth 4 (kernel template in decode_kernel.h).
+// depth 3, or 4 for per-token blocks (kernel template in decode_kernel.h).
 #include "decode_kernel.h"
 
 namespace mqa {

@@ -644,8 +644,8 @@ hipError_t launch_rgdb(const DecodeLaunch &p, const DecodeArgs &a, int grid, hip
 // The kernels a (rows per wave R, waves G, head tiles HT, mode, head dim)
 // launch can take, by block size and ring depth: 64-token blocks at 32 heads
 // and head dim 128 take ring depths 2..7 for the logits call and 3 for the
-// fused top-k's modes; every other layout takes depth 4.  (Q and weights of
-// a wave's rows stay in VGPRs, so R HT <= 4.)
+// fused top-k's modes; per-token blocks take depth 4 and every other layout
+// depth 3.  (Q and weights of a wave's rows stay in VGPRs, so R HT <= 4.)
 template <int R, int G, int HT, int MODE, int DIM = kDim>
 hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipStream_t stream)
 {
@@ -670,17 +670,17 @@ hipError_t launch_rg(const DecodeLaunch &p, const DecodeArgs &a, int grid, hipSt
                 }
             }
         }
-        if (p.depth != 4)
+        if (p.depth != (p.block_size == 1 ? 4 : 3))
             return hipErrorInvalidValue;
         switch (p.block_size) {
         case 1: return launch_rgdb<R, G, 4, 1, HT, MODE, DIM>(p, a, grid, stream);
-        case 16: return launch_rgdb<R, G, 4, 16, HT, MODE, DIM>(p, a, grid, stream);
+        case 16: return launch_rgdb<R, G, 3, 16, HT, MODE, DIM>(p, a, grid, stream);
         case 64:
             if constexpr (HT > 1 || DIM != kDim)
-                return launch_rgdb<R, G, 4, 64, HT, MODE, DIM>(p, a, grid, stream);
+                return launch_rgdb<R, G, 3, 64, HT, MODE, DIM>(p, a, grid, stream);
             else
                 return hipErrorInvalidValue;  // handled above
-        case 128: return launch_rgdb<R, G, 4, 128, HT, MODE, DIM>(p, a, grid, stream);
+        case 128: return launch_rgdb<R, G, 3, 128, HT, MODE, DIM>(p, a, grid, stream);
         default: return hipErrorInvalidValue;
         }
     }

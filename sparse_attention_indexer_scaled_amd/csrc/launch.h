@@ -43,8 +43,8 @@ struct DecodeLaunch {
     int depth;     // 64-token steps in each workgroup's LDS ring, 2..7 (at most 64 KiB);
                    // 4 for block sizes other than 64
     int block_size;  // tokens per cache block: 1, 16, 64 or 128
-    int head_tiles;  // num_heads / 32: 1, 2 or 4 (2 and 4: depth 4)
-    int head_dim;    // 128, or 64 (blocks of 16 or more tokens, depth 4)
+    int head_tiles;  // num_heads / 32: 1, 2 or 4
+    int head_dim;    // 128 or 64
     int tiled;       // 1: K rows in the preshuffled (16,16) order (block size >= 16)
     // fused top-k only (zero / NULL for the logits call):
     int mode;              // 0 logits, 1 sample, 2 filter (modes 1, 2: the default depth,

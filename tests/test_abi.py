@@ -125,7 +125,7 @@ def test_decode_validation(lib):
     for bs in (1, 16, 64, 128):  # head dim 64: every block size
         assert _decode(lib, nulls, D=64, bs=bs) == mqa._native.MQA_ERR_INVALID_ARG  # NULLs
         assert "NULL" in mqa.last_error()
-    bad = _native.Tunables(ring_depth=3)  # head dim 64: ring depth 0 or 4
+    bad = _native.Tunables(ring_depth=4)  # head dim 64: ring depth 0 or 3
     assert _decode(lib, nulls, D=64, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
     assert "ring_depth" in mqa.last_error()
     for H in (64, 128):
@@ -144,8 +144,12 @@ def test_decode_validation(lib):
     assert _decode(lib, nulls) == mqa._native.MQA_ERR_INVALID_ARG
     odd = [P(0x2002)] * 6
     assert _decode(lib, odd) == mqa._native.MQA_ERR_INVALID_ARG
-    bad = _native.Tunables(ring_depth=3)  # other depths only with 64-token blocks
+    bad = _native.Tunables(ring_depth=4)  # other depths only with 64-token blocks
     assert _decode(lib, nulls, bs=16, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "ring_depth" in mqa.last_error()
+    bad = _native.Tunables(ring_depth=3)  # per-token blocks: 0 or 4
+    assert _decode(lib, nulls, bs=1, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
+    assert "ring_depth" in mqa.last_error()
     for bad in (_native.Tunables(rows_per_block=5), _native.Tunables(ring_depth=1),
                 _native.Tunables(ring_depth=8), _native.Tunables(num_warps=2),
                 _native.Tunables(split_kv=-1)):
@@ -193,19 +197,19 @@ def test_fused_topk_validation(lib):
     assert _fused(lib, nulls, D=96) == E.MQA_ERR_UNSUPPORTED
     assert _fused(lib, nulls, D=64, bs=1) == E.MQA_ERR_INVALID_ARG  # head dim 64: NULLs
     assert _fused(lib, nulls, D=64) == E.MQA_ERR_INVALID_ARG
-    assert _fused(lib, nulls, D=64, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
+    assert _fused(lib, nulls, D=64, tun=ctypes.byref(E.Tunables(ring_depth=4))) == \
         E.MQA_ERR_INVALID_ARG
     assert "ring depth" in mqa.last_error()
     for H, bs in ((64, 64), (128, 64), (32, 16), (32, 1), (32, 128), (64, 16), (128, 1)):
         assert _fused(lib, nulls, H=H, bs=bs) == E.MQA_ERR_INVALID_ARG
         assert "NULL" in mqa.last_error()
-    # the ring depth is the logits call's default: 3 for 64-token blocks at 32 heads, else 4
+    # the ring depth is the logits call's default: 4 for per-token blocks, else 3
     assert _fused(lib, nulls, tun=ctypes.byref(E.Tunables(ring_depth=4))) == E.MQA_ERR_INVALID_ARG
     assert "ring depth" in mqa.last_error()
-    assert _fused(lib, nulls, bs=16, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
+    assert _fused(lib, nulls, bs=1, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
         E.MQA_ERR_INVALID_ARG
     assert "ring depth" in mqa.last_error()
-    assert _fused(lib, nulls, bs=16, tun=ctypes.byref(E.Tunables(ring_depth=4))) == \
+    assert _fused(lib, nulls, bs=16, tun=ctypes.byref(E.Tunables(ring_depth=3))) == \
         E.MQA_ERR_INVALID_ARG
     assert "NULL" in mqa.last_error()
     assert _fused(lib, nulls, B=0) == 0          # nothing to do, nothing dereferenced
