@@ -386,16 +386,26 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """Source text without comments and blank lines, so that a profile stays
+    valid across comment edits (a '//' inside a string literal is dropped as
+    well; that only affects the hash)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def source_hash(kernel):
     """Hash of one kernel's sources (with the host launcher that picks its
-    launch shape) and the device build flags: a profile is only reported while
-    it matches the code being timed."""
+    launch shape; comments ignored) and the device build flags: a profile is
+    only reported while it matches the code being timed."""
     import hashlib
     from sparse_attention_indexer_scaled_amd import build
     h = hashlib.sha256(" ".join(build.DEVICE).encode())
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(build.CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(build.CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,6 @@
-// Paged decode kernel template (gfx950), shared by the logits call (decode.hip)
-// and the fused top-k's sample and filter modes (decode_fused.hip).
+// Paged decode kernel template (gfx950), shared by the logits call (decode.hip,
+// decode_heads.hip, decode_d64.hip) and the fused top-k's sample and filter
+// modes (decode_fused.hip, decode_fused_d64.hip).
 //
 // What it computes (aiter PR 5047 page, "Motivation" and "Technical Details"):
 // row j of sequence b gets  sum_h relu(<Q[b,j,h,:], K[p,:]>) * w[b,j,h] * scale[p]
@@ -9,23 +10,26 @@
 // Work decomposition.  A workgroup owns one (sequence b, KV split s) and walks
 // the split's 64-token steps (one cache block each) in order.  Its G waves are
 // row groups: wave g holds rows [g R, g R + R) of the sequence's next_n rows
-// (Q: 16 VGPR per row, head weights: 16 VGPR per row, for the wave's whole
-// life).  All rows of the sequence share ONE K stream (both pages, "Technical
+// (Q: DIM / 8 VGPR per row and head tile, head weights: 16 VGPR per row and
+// head tile, for the wave's whole life).  All rows of the sequence share ONE K stream (both pages, "Technical
 // Details": rows share one K stream; the next_n-tiling issue page asks for
 // next_n folded into the tile rather than into the program count):
 //
 //   - K and scales travel HBM -> LDS by direct loads (global_load_lds, no
-//     VGPRs) into a ring of D slots, each slot one cache block (8 KiB of K in a
-//     bank-conflict-free order + 256 B of scales).  Step k+D-1 is requested
-//     while step k computes, so D-1 blocks per workgroup are always in flight
-//     and the ring, not the register file, holds the bytes in flight.
-//   - The G waves split each block's nine load instructions between them,
-//     then every wave reads the whole block from LDS (ds_read_b128) into the
-//     MFMA operand layout.  One s_barrier per step publishes the block to all
-//     waves and retires the slot the next request overwrites.
-//   - Per 32-token tile and row: two fp8 MFMAs, the in-lane relu.weight sum
-//     over 16 heads, one permlane32 swap + add per row pair, kv_scale once per
-//     column (the hoist: kv_scale >= 0, relu positive-homogeneous).
+//     VGPRs) into a ring of D slots, each slot one 64-token step (64 DIM bytes
+//     of K in a bank-conflict-free order + 256 B of scales).  Step k+D-1 is
+//     requested while step k computes, so D-1 steps per workgroup are always
+//     in flight and the ring, not the register file, holds the bytes in
+//     flight.
+//   - The G waves split each step's loads (DIM / 16 chunks of 1 KiB and the
+//     scales) between them, then every wave reads the whole step from LDS
+//     (ds_read_b128) into the MFMA operand layout.  One s_barrier per step
+//     publishes the step to all waves and retires the slot the next request
+//     overwrites.
+//   - Per 32-token tile, row and 32-head tile: DIM / 64 fp8 MFMAs and the
+//     in-lane relu.weight sum over 16 heads; per row pair one permlane32 swap
+//     + add, then kv_scale once per column (the hoist: kv_scale >= 0, relu
+//     positive-homogeneous).
 //   - A step's results are stored one step later, after that step's request
 //     and LDS reads, so the stores retire while the next step computes.
 //     (Stored before the request, they lead the compiler to wait for every
