@@ -8,8 +8,6 @@
 
 namespace mqa {
 
-int decode_ring_bytes(int depth) { return depth * kSlotBytes; }
-
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream)
 {
     if (p.mode != kLogits)

@@ -61,7 +61,6 @@ template <int DIM>
 constexpr int k_chunks() { return kStep * DIM / 1024; }
 template <int DIM>
 constexpr int rows_per_chunk() { return 1024 / DIM; }
-constexpr int kSlotBytes = slot_bytes<kDim>();  // 8448 bytes at head dim 128
 constexpr int kSampleChunks = kFusedSampleChunks;
 constexpr int kSampleSteps = kFusedSampleSteps;
 constexpr int kSampleCols = kFusedSampleCols;
@@ -73,7 +72,6 @@ constexpr int ring_lds_bytes()
 {
     return D * slot_bytes<DIM>() + (BS == 1 ? (2 * D - 2) * kStep * 4 : 0);
 }
-constexpr int kChunks = k_chunks<kDim>() + 1;  // 8 x 1 KiB of K + 1 x 256 B of scales
 
 // Sizes and launch shape; the pointers are separate __restrict__ kernel
 // arguments so the compiler may read the block table with scalar loads.

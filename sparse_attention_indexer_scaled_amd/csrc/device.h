@@ -30,8 +30,7 @@ constexpr int kHeads = 32;
 constexpr int kDim = 128;
 constexpr int kTile = 32;  // tokens per MFMA column tile
 constexpr int kStep = 64;  // tokens per wave step: two tiles
-constexpr int kBlock = 64; // paged-cache block size supported by the decode kernel
-constexpr int kBlockBytes = kBlock * (kDim + 4);
+constexpr int kBlock = 64; // cache block size whose blocks are exactly one step
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));

@@ -142,8 +142,6 @@ struct KcacheLaunch {
     int tiled;            // 1: K rows in the preshuffled (16,16) order
 };
 
-// Bytes of LDS a decode workgroup uses for a ring of `depth` blocks.
-int decode_ring_bytes(int depth);
 
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
