@@ -1049,14 +1049,37 @@ __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
     __syncthreads();
     int n;
     if (ok) {  // uniform
-        // segment s starts at the first column of the filter workgroup s
-        for (int sgm = wave; sgm < split; sgm += kWaves) {
-            const int m = cnt[sgm];
-            const int64_t col0 = (int64_t)nsteps * sgm / split * 64;
-            const int dst = (int)sh.hist[sgm];
-            for (int i = lane; i < m; i += 64)
-                sh.buf[dst + i] = row[col0 + i];
+        // Entry i (in segment order) belongs to the last segment whose prefix
+        // is <= i (empty segments share their successor's prefix); segment s
+        // starts at the first column of the filter workgroup s.  Every thread
+        // first finds the sources of its entries, then issues all their loads,
+        // so the gather costs one round of memory latency, not one per segment.
+        constexpr int EPT = kSortCap / kThreads;
+        int64_t src[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = tid + e * kThreads;
+            src[e] = -1;
+            if (i < total) {
+                int lo = 0, hi = split - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if ((int)sh.hist[mid] <= i)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                src[e] = (int64_t)nsteps * lo / split * 64 + (i - (int)sh.hist[lo]);
+            }
         }
+        uint64_t v[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            v[e] = src[e] >= 0 ? row[src[e]] : 0ull;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (src[e] >= 0)
+                sh.buf[tid + e * kThreads] = v[e];
         n = total;
     } else {
         // the row's own segment region (>= mml floats) now holds its logits
