@@ -172,7 +172,7 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     // faster than 8 rows (1 wave per SIMD) on the long chunk although K is
     // re-read from L2 twice as often: M 4096, N 32768 took 525 against 536 us
     // at head dim 128 and 356 against 384 us at head dim 64 (means of three
-    // alternating runs on one box).  High-m first for long causal chunks
+    // alternating runs on one MI355X).  High-m first for long causal chunks
     // (aiter PR 5046 page, "Technical Details": N > 2048).
     //   Small problems (at most 16384 row-steps, e.g. 64 rows x 512
     //   columns) are latency-bound: one row and one wave per workgroup and
@@ -189,7 +189,7 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
         p.split_n = t.split_n;
     } else {
         // ~2048 workgroups; ~8192 at head dim 64 (split 8 on the long chunk: 355
-        // against 366 us with split 2, three alternating runs on one box)
+        // against 366 us with split 2, three alternating runs on one MI355X)
         int64_t want = std::max<int64_t>(1, ceil_div(head_dim == 64 ? 8192 : 2048, nrb));
         int64_t cap = std::max<int64_t>(1, steps / ((small ? 2 : 4) * p.num_warps));
         p.split_n = (int)std::min(want, cap);
