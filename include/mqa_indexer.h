@@ -165,11 +165,11 @@ int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, const float *
  * sequence's context may hold any bytes (NaN included): they never reach an
  * output.
  * kv_block_size 1, 16, 64 or 128 at 32, 64 or 128 heads and head_dim 128 or
- * 64 (a block of bs tokens is then bs * 68 bytes).  The ring_depth tunable
- * takes 0 or the layout's one depth (4 for kv_block_size 1, else 3), except
- * with
- * kv_block_size 64, 32 heads and head_dim 128.  kv_layout MQA_KV_SLOT_MAJOR
- * or MQA_KV_PRESHUFFLED (the latter not with kv_block_size 1).
+ * 64 (at head_dim 64 a block of bs tokens is bs * 68 bytes).  The ring_depth
+ * tunable takes 2..7 with kv_block_size 64, 32 heads and head_dim 128, and
+ * otherwise 0 or the layout's one depth (4 for kv_block_size 1, else 3).
+ * kv_layout MQA_KV_SLOT_MAJOR or MQA_KV_PRESHUFFLED (the latter not with
+ * kv_block_size 1).
  * batch == 0 or max_model_len == 0 is a successful no-op.  next_n outside 1..8,
  * a bad kv_layout, negative sizes, NULL or misaligned pointers ->
  * MQA_ERR_INVALID_ARG; a shape, block size or layout outside the gate ->
