@@ -54,3 +54,30 @@ def test_generator_is_seeded():
     b = inputs.make_decode(2, 2, None, 4096, seed=5, ctx_range=(100, 4000))
     assert np.array_equal(a.kv_cache, b.kv_cache) and np.array_equal(a.block_tables, b.block_tables)
     assert np.array_equal(a.q, b.q) and np.array_equal(a.weights, b.weights)
+
+
+def test_decode_bytes_at_head_dim_64_by_hand():
+    """Workload 21 (the headline shape at head dim 64), term by term: 68-byte
+    tokens, every output element once, Q, weights, used table entries and
+    context lengths."""
+    B, nn, ctx, H, D = 16, 6, 131072, 32, 64
+    want = (B * ctx * (64 + 4)          # K + scale per cached token
+            + B * nn * ctx * 4          # fp32 logits, -inf fill included
+            + B * nn * H * D            # fp8 Q
+            + B * nn * H * 4            # fp32 weights
+            + B * (ctx // 64) * 4       # used table entries
+            + B * 4)                    # context lengths
+    assert workload.decode_essential_bytes(B, nn, [ctx] * B, ctx, H=H, D=D) == want
+    d = inputs.make_config(21)
+    assert d.D == 64 and d.kv_cache.shape[1] == 64 * 68
+
+
+def test_cache_pack_roundtrip_head_dim_64_per_token_blocks():
+    """68-byte per-token records: token p's 64 K bytes, then its scale."""
+    d = inputs.make_decode(2, 1, [5, 9], 16, seed=11, D=64, block_size=1)
+    kview, sview = inputs.cache_views(d.kv_cache, 1, 64)
+    assert d.kv_cache.shape[1] == 68
+    for b in range(2):
+        for p in range(int(d.context_lens[b])):
+            blk = d.block_tables[b, p]
+            assert np.array_equal(kview[blk, 0], d.k_seq[b][p]) and sview[blk, 0] == d.s_seq[b][p]
