@@ -43,6 +43,24 @@ def test_hand_example_insert():
     assert np.array_equal(out, want)
 
 
+def test_negative_extreme_sets_the_scale():
+    """Worked by hand: the largest magnitude is -448, so amax = 448, the scale is
+    448 / 448 = 1 and the codes are the format's own: -448 = -1.75 * 2^8 is sign 1,
+    exponent field 15, mantissa 6 (0xFE); 1 = 2^0 is exponent field 7 (0x38); 0 is 0x00."""
+    k = np.zeros((1, 128), np.float32)
+    k[0, 0], k[0, 1] = -448.0, 1.0
+    codes, scale = kcache.quantize_tokens(k)
+    assert scale.tolist() == [1.0]
+    assert codes[0, :3].tolist() == [0xFE, 0x38, 0x00] and not codes[0, 3:].any()
+
+
+def test_all_zero_token():
+    """A zero row takes the floor of the amax: codes 0 and the scale of amax 1e-12."""
+    codes, scale = kcache.quantize_tokens(np.zeros((1, 64), np.float32))
+    assert not codes.any()
+    assert scale[0] == np.float32(np.float32(1e-12) / np.float32(448.0))
+
+
 def _boundaries():
     """Every midpoint between adjacent e4m3fn values, one fp32 ulp either
     side, and the values themselves, both signs."""
