@@ -33,3 +33,29 @@ def test_every_kernel_has_a_source_hash():
     for w in ("decode_B16_nn6_ctx131072", "prefill_M4096_N32768", "topk_k2048_x",
               "kcache_insert_T4096_fp32", "decode_topk_k2048_x"):
         assert bench.kernel_of(w) in hashes
+
+
+def _profile_hash(path):
+    if path.endswith(".json"):
+        import json
+        with open(path) as f:
+            return json.load(f)["source_hash"]
+    with open(path) as f:
+        return [l for l in f if l.startswith("# source_hash")][0].split(":", 1)[1].strip()
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    """Every summary under profiles/ was taken from the kernel code as it stands
+    (comments aside): a kernel change calls for fresh profiles."""
+    pdir = os.path.join(ROOT, "profiles")
+    names = sorted(os.listdir(pdir))
+    assert names
+    for name in names:
+        if name.endswith(("_traffic.json", "_counters.json")):
+            workload = name[: name.rfind("_")]
+        elif name.endswith("_kernel_stats.txt"):
+            workload = name[: -len("_kernel_stats.txt")]
+        else:
+            raise AssertionError("unexpected file under profiles/: %s" % name)
+        want = bench.source_hash(bench.kernel_of(workload))
+        assert _profile_hash(os.path.join(pdir, name)) == want, "stale profile %s" % name
