@@ -15,7 +15,10 @@ to a per-token fp32 dequant scale in the paged cache (aiter PR 5047 page,
 and the token's 128 code bytes and 4 scale bytes go to its slot of the
 block-split cache layout (block i = bs*(D+4) bytes: the bs K rows, slot-major,
 then the bs fp32 scales).  Tokens whose slot is negative are padding and write
-nothing.  e4m3fn_rne picks the representable value nearest to its argument,
+nothing; so do tokens whose slot lies at or past the cache's last slot
+(num_blocks * bs).  The pages name no out-of-range rule: the reading taken is
+that such a token has no slot to go to and is dropped, like padding, rather
+than written past the cache.  e4m3fn_rne picks the representable value nearest to its argument,
 ties to the code with the even mantissa, keeping the sign (a negative value
 that rounds to zero gives -0, code 0x80); the representable values come from
 the format definition (``oracle.e4m3fn_table``, the C decoder).
@@ -73,7 +76,8 @@ def quantize_tokens(k: np.ndarray):
 def insert(kv_cache: np.ndarray, k: np.ndarray, slot_mapping: np.ndarray, block_size: int,
            preshuffle: bool = False):
     """Return a copy of kv_cache [num_blocks, bs*(D+4)] bytes with the tokens
-    of k [T, D] quantised into their slots (slot < 0: token skipped).
+    of k [T, D] quantised into their slots (slot < 0 or slot >=
+    num_blocks * block_size: token skipped).
 
     preshuffle: the K rows of a block are in 16 x 16-byte tiles (the decode
     oracle's layout 1): byte d of slot s at (s/16)*16*D + (d/16)*256 +
@@ -82,9 +86,10 @@ def insert(kv_cache: np.ndarray, k: np.ndarray, slot_mapping: np.ndarray, block_
     T, D = k.shape
     codes, scale = quantize_tokens(k)
     flat = cache.reshape(cache.shape[0], -1)
+    num_slots = cache.shape[0] * block_size
     for t in range(T):
         s = int(slot_mapping[t])
-        if s < 0:
+        if s < 0 or s >= num_slots:
             continue
         blk, slot = divmod(s, block_size)
         if preshuffle:

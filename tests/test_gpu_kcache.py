@@ -70,6 +70,23 @@ def test_insert_preshuffled_layout(bs, bf16):
         raise AssertionError("%d bytes differ, first at %s" % (len(diff), diff[0].tolist()))
 
 
+@pytest.mark.parametrize("bs", [1, 16, 64])
+def test_insert_skips_slots_past_the_cache(bs):
+    """Slots at or past num_blocks * block_size are dropped like padding (the
+    oracle's reading of the out-of-range rule); the whole cache is compared."""
+    c = inputs.make_kcache_insert(300, -(-300 // bs) + 2, seed=660 + bs, block_size=bs)
+    nslots = c.kv_cache.shape[0] * bs
+    slots = c.slot_mapping.copy()
+    slots[0:6] = [nslots, nslots + 1, nslots + bs, 2 * nslots, 1 << 40, (1 << 62) + 5]
+    c = inputs.KcacheInsertInputs(c.k, slots, c.kv_cache, bs, c.bf16)
+    say("kcache insert out-of-range slots bs=%d" % bs)
+    got = gpu_insert(c)
+    want = oracle_kcache.insert(c.kv_cache, c.k, c.slot_mapping, bs)
+    if not np.array_equal(got, want):
+        diff = np.argwhere(got != want)
+        raise AssertionError("%d bytes differ, first at %s" % (len(diff), diff[0].tolist()))
+
+
 def test_rounding_boundaries_on_gpu():
     """Rows whose quotients land on every e4m3fn rounding boundary: the row
     maximum is 448 so the scale is 1 and k / scale = k exactly."""

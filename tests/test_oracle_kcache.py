@@ -43,6 +43,25 @@ def test_hand_example_insert():
     assert np.array_equal(out, want)
 
 
+def test_hand_example_out_of_range_slot_is_skipped():
+    g, k, codes, _ = _golden()
+    cache = np.arange(3 * 16, dtype=np.uint8).reshape(3, 16)
+    slots = np.array([int(t) for t in g["slots_oob"]], dtype=np.int64)
+    out = kcache.insert(cache, k, slots, block_size=2)
+    want = cache.copy()
+    want[2, 0:4] = codes[1]
+    want[2, 8:12] = [0x00, 0x00, 0x00, 0x3f]
+    assert np.array_equal(out, want)
+
+
+def test_slots_past_the_cache_write_nothing():
+    rng = np.random.default_rng(15)
+    cache = rng.integers(0, 256, (2, 16 * 132), dtype=np.uint8)
+    k = rng.standard_normal((3, 128)).astype(np.float32)
+    out = kcache.insert(cache, k, np.array([32, 33, 1 << 40], np.int64), 16)
+    assert np.array_equal(out, cache)
+
+
 def test_negative_extreme_sets_the_scale():
     """Worked by hand: the largest magnitude is -448, so amax = 448, the scale is
     448 / 448 = 1 and the codes are the format's own: -448 = -1.75 * 2^8 is sign 1,

@@ -143,7 +143,8 @@ _PY_MUTANTS = {
     "kcache scale slot": (kcache, kcache_pins, "off = block_size * D + 4 * slot",
                           "off = block_size * D + 4 * ((slot + 1) % block_size)"),
     "kcache tile stride": (kcache, kcache_pins, "(d // 16) * 256", "(d // 16) * 128"),
-    "kcache padding written": (kcache, kcache_pins, "if s < 0:", "if s < -1:"),
+    "kcache padding written": (kcache, kcache_pins, "if s < 0 or", "if s < -1 or"),
+    "kcache last slot written": (kcache, kcache_pins, "s >= num_slots:", "s > num_slots:"),
 }
 
 
