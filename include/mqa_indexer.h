@@ -241,6 +241,31 @@ int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const f
                           int max_blocks_per_seq, int max_model_len, int k, void *workspace,
                           size_t workspace_bytes, const mqa_tunables *tun, hipStream_t stream);
 
+/*
+ * paged_mqa_topk_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call without the workspace arguments.  The workspace
+ * lives in a static device array of MQA_NOALLOC_SCRATCH_BYTES held by the
+ * library (one copy per device it runs on, kept until the process ends), so
+ * the call makes no allocation of its own; the caller still owns the inputs
+ * and `indices`.  Every call on one device shares that array: calls that
+ * overlap on a device (several streams or threads) race.  Nothing in it has to
+ * start cleared, so a call depends on no earlier call's contents.
+ *
+ * Errors as for paged_mqa_topk_decode, plus: a problem whose
+ * paged_mqa_topk_workspace_size exceeds MQA_NOALLOC_SCRATCH_BYTES (checked
+ * first; 128 MiB holds 96 rows of 131072 positions) -> MQA_ERR_INVALID_ARG;
+ * the array's device address not available -> MQA_ERR_DEVICE.
+ */
+#define MQA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int paged_mqa_topk_decode_noalloc(const uint8_t *q_fp8, const uint8_t *kv_cache,
+                                  const float *weights, const int32_t *context_lens,
+                                  const int32_t *block_tables, int32_t *indices, int batch,
+                                  int next_n, int num_heads, int head_dim, int kv_block_size,
+                                  int kv_layout, int num_blocks, int max_blocks_per_seq,
+                                  int max_model_len, int k, const mqa_tunables *tun,
+                                  hipStream_t stream);
+
 /* Workspace bytes paged_mqa_topk_decode needs (0 for sizes it rejects or
  * treats as a no-op).  Host-only, never fails. */
 size_t paged_mqa_topk_workspace_size(int batch, int next_n, int max_model_len);

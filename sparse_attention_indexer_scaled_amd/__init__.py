@@ -22,6 +22,7 @@ from ._native import (  # noqa: F401
     mqa_logits_prefill,
     paged_mqa_logits_decode,
     paged_mqa_topk_decode,
+    paged_mqa_topk_decode_noalloc,
     paged_mqa_topk_workspace_size,
     topk_indices,
 )

@@ -24,8 +24,10 @@ MQA_ERR_LAUNCH = -3
 MQA_ERR_DEVICE = -4
 
 EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode",
-            "mqa_topk_indices", "paged_mqa_topk_decode", "paged_mqa_topk_workspace_size",
-            "mqa_kcache_quantize_insert", "mqa_last_error")
+            "mqa_topk_indices", "paged_mqa_topk_decode", "paged_mqa_topk_decode_noalloc",
+            "paged_mqa_topk_workspace_size", "mqa_kcache_quantize_insert", "mqa_last_error")
+# bytes of the library's static scratch (MQA_NOALLOC_SCRATCH_BYTES in the header)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 MQA_DTYPE_FP32 = 0
 MQA_DTYPE_BF16 = 1
 MQA_KV_SLOT_MAJOR = 0
@@ -72,6 +74,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_mqa_topk_decode.restype = I
     lib.paged_mqa_topk_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P,
                                           ctypes.c_size_t, P, P]
+    lib.paged_mqa_topk_decode_noalloc.restype = I
+    lib.paged_mqa_topk_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I,
+                                                  P, P]
     lib.paged_mqa_topk_workspace_size.restype = ctypes.c_size_t
     lib.paged_mqa_topk_workspace_size.argtypes = [I, I, I]
     lib.mqa_kcache_quantize_insert.restype = I
@@ -247,6 +252,37 @@ def paged_mqa_topk_decode(q_fp8: torch.Tensor, kv_cache: torch.Tensor, weights: 
         B, next_n, H, D, int(kv_block_size), _layout(preshuffle), cache.shape[0],
         block_tables.shape[1], int(max_model_len), int(k), _dev(ws, "workspace"), ws.numel(),
         _tun(tunables), _stream(stream, q.device))
+    _check(rc)
+    return indices
+
+
+def paged_mqa_topk_decode_noalloc(q_fp8: torch.Tensor, kv_cache: torch.Tensor,
+                                  weights: torch.Tensor, context_lens: torch.Tensor,
+                                  block_tables: torch.Tensor, max_model_len: int, k: int,
+                                  indices: torch.Tensor, kv_block_size: int = 64,
+                                  tunables: Optional[Tunables] = None, stream=None,
+                                  preshuffle: bool = False) -> torch.Tensor:
+    """paged_mqa_topk_decode with the library's static scratch as its
+    workspace: no device allocation in the call (the caller passes
+    `indices`, [B*next_n, k] int32).  Calls that overlap on one device race."""
+    q = _bytes(q_fp8, "q_fp8")
+    cache = _bytes(kv_cache, "kv_cache")
+    B, next_n, H, D = q.shape
+    if cache.dim() != 2 or cache.shape[1] != kv_block_size * (D + 4):
+        raise ValueError("kv_cache must be [num_blocks, kv_block_size*(head_dim+4)] bytes")
+    if weights.shape != (B * next_n, H) or context_lens.shape != (B,):
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks_per_seq]")
+    if indices.shape != (B * next_n, k):
+        raise ValueError("indices must be [B*next_n, k]")
+    rc = load_library().paged_mqa_topk_decode_noalloc(
+        _dev(q, "q_fp8"), _dev(cache, "kv_cache"), _dev(weights, "weights", torch.float32),
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), _dev(indices, "indices", torch.int32),
+        B, next_n, H, D, int(kv_block_size), _layout(preshuffle), cache.shape[0],
+        block_tables.shape[1], int(max_model_len), int(k), _tun(tunables),
+        _stream(stream, q.device))
     _check(rc)
     return indices
 

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -432,6 +433,76 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
     if (e != hipSuccess)
         return fail(MQA_ERR_LAUNCH, "fused top-k launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+// Device scratch of the allocation-free fused top-k (paged_mqa_topk_decode_noalloc):
+// the workspace paged_mqa_topk_decode takes from its caller, held by the library
+// instead.  Every device the library runs on holds one copy at its own address
+// until the process ends.  128 MiB covers 96 rows of 131072 positions (about 8
+// bytes per row and position).
+constexpr size_t kNoAllocScratchBytes = MQA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device; guarded by g_scratch_mu
+
+// The device address of `scratch` on the current device, looked up once per
+// device (the host-side name `scratch` is only a stand-in for it).
+int scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(MQA_ERR_DEVICE, "no usable HIP device");
+    }
+    if (dev >= kMaxDevices)
+        return fail(MQA_ERR_DEVICE, "device %d is past the %d devices the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(MQA_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MQA_OK;
+}
+
+} // namespace
+
+extern "C" int paged_mqa_topk_decode_noalloc(const uint8_t *q_fp8, const uint8_t *kv_cache,
+                                             const float *weights, const int32_t *context_lens,
+                                             const int32_t *block_tables, int32_t *indices,
+                                             int batch, int next_n, int num_heads, int head_dim,
+                                             int kv_block_size, int kv_layout, int num_blocks,
+                                             int max_blocks_per_seq, int max_model_len, int k,
+                                             const mqa_tunables *tun, hipStream_t stream)
+{
+    const size_t need = paged_mqa_topk_workspace_size(batch, next_n, max_model_len);
+    if (need > kNoAllocScratchBytes)
+        return fail(MQA_ERR_INVALID_ARG, "batch %d x next_n %d rows of max_model_len %d need %zu "
+                    "bytes of scratch; the library's static scratch holds %zu", batch, next_n,
+                    max_model_len, need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        if (int rc = check_device())
+            return rc;
+        if (int rc = scratch_of_current_device(&ws))
+            return rc;
+    }
+    // Nothing in the workspace has to start at zero: every word a kernel reads
+    // was written earlier in the same call.
+    return paged_mqa_topk_decode(q_fp8, kv_cache, weights, context_lens, block_tables, indices,
+                                 batch, next_n, num_heads, head_dim, kv_block_size, kv_layout,
+                                 num_blocks, max_blocks_per_seq, max_model_len, k, ws,
+                                 kNoAllocScratchBytes, tun, stream);
 }
 
 extern "C" int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *indices,
