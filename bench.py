@@ -1,23 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the lightning-indexer logits library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--hot]
-                    [--no-cpu] [--only IDX] [--calib-copy MB]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--workload IDX]
+                    [--hot] [--no-cpu] [--only IDX] [--calib-copy MB] [--calib-mfma]
 
 A step is one call of the op over one batch of synthetic input (every stage of
 the kernel: Q/weights prologue, K load or block-table gather, fp8 MFMA,
 relu.weight epilogue, lane-permute head reduce, kv-scale, masked store and
 -inf fill).  The headline line is paged decode, batch 16, next_n 6, context
 131072, 64-token blocks (the workload the pages' own decode timings are quoted
-on); the other four named workloads are measured in the same run and reported
+on); the other named workloads are measured in the same run and reported
 under "workloads".
 
-Timing: W eager warm-up calls (extended to ~0.3 s so clocks settle), then
-exactly K calls between two events on the launch stream, with synchronisation
-on both sides: replayed from one HIP graph when a call is launch-bound (under
-20 us), plain back-to-back launches otherwise.  Inputs rotate over enough copies that the
-working set exceeds the 256 MB MALL (cold, as a serving step sees per-layer
-KV); --hot keeps one copy.
+Timing: W eager warm-up calls (extended to ~0.3 s so clocks settle), then R
+timings of exactly K calls, each between two events on the launch stream with
+synchronisation on both sides; the median of the R per-call times is
+reported (the repeats beside it).  A call is replayed from one HIP graph when
+it is launch-bound (under 20 us), timed as plain back-to-back launches
+otherwise.  Inputs rotate over enough copies that the working set exceeds the
+256 MB MALL (cold, as a serving step sees per-layer KV); the five named
+configurations (and the next_n 1 long-context decode) are also timed on one
+copy (hot); --hot keeps one copy throughout.
+
+Measured in the same run: the launch floor (an empty kernel timed the same
+two ways), the fp8 MFMA rate of an MFMA-only kernel (the roofline's peak stays
+the published 5.0 PFLOP/s; the measured rate is reported beside it), and the
+CPU oracle's time on each named configuration (median of three runs on the
+short ones, one run on the long prefill chunk's row sample and the ragged
+batch).
 
 Prints ONE JSON line.
 """
@@ -62,6 +72,10 @@ def parse():
                     help="WORKLOAD DIR [DIR ...]: summarise rocprofv3 --pmc runs of SQ/GRBM "
                          "counters into profiles/ (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timings of --steps calls per workload; the median is reported")
+    ap.add_argument("--calib-mfma", action="store_true",
+                    help="only time the MFMA-only calibration kernel (fp8 TFLOP/s)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -87,6 +101,12 @@ KCACHE_WORKLOADS = {7: (4096, False), 8: (96, True)}
 # Fused decode top-k workloads: index -> (decode workload, k); the indices
 # only, the logits never written.
 FUSED_WORKLOADS = {16: (2, 2048), 17: (2, 512)}
+# Workloads also timed on one input copy (MALL-warm) beside the cold figure.
+HOT_ALSO = (0, 1, 2, 3, 4, 22)
+# Workloads whose oracle time is measured in the same run: index -> runs
+# (median of three on the short ones, one run on the long prefill chunk's row
+# sample and the ragged batch).
+CPU_BASELINE_RUNS = {0: 3, 1: 3, 2: 3, 3: 1, 4: 1}
 
 
 class Workload:
@@ -256,10 +276,12 @@ def make_workload(idx, hot, tunables=None):
     return Workload(idx, hot, tunables)
 
 
-def time_workload(wl, steps, warmup, graph=None, settle_s=0.3):
-    """Per-call milliseconds of exactly `steps` calls.  Warm-up: `warmup`
-    calls, extended until about settle_s of GPU work has run so that clocks
-    have left their idle state before the timed region."""
+def time_workload(wl, steps, warmup, graph=None, settle_s=0.3, repeats=5):
+    """Per-call milliseconds: `repeats` timings of exactly `steps` calls, each
+    between two events on the launch stream with a synchronisation on both
+    sides; returns (median, list of the repeats).  Warm-up: `warmup` calls,
+    extended until about settle_s of GPU work has run so that clocks have
+    left their idle state before the timed region."""
     import torch
     t0 = time.time()
     i = 0
@@ -295,26 +317,30 @@ def time_workload(wl, steps, warmup, graph=None, settle_s=0.3):
         stream.wait_stream(side)
         g.replay()  # one untimed replay so the graph itself is resident
         torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    if graph:
-        g.replay()
-    else:
-        for i in range(steps):
-            wl.call(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    return ms / steps
+    reps = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        if graph:
+            g.replay()
+        else:
+            for i in range(steps):
+                wl.call(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        reps.append(start.elapsed_time(end) / steps)
+    return float(np.median(reps)), reps
 
 
-def summarize(wl, ms):
+def summarize(wl, ms, reps=()):
     us = ms * 1e3
     d = dict(workload=wl.cfg["name"], us_per_call=round(us, 3), input_copies=wl.nsets,
              timing="hip graph replay" if wl.graph else "back-to-back launches",
              essential_bytes=int(wl.bytes), valid_pairs=int(wl.pairs))
+    if reps:
+        d["repeats_us"] = [round(r * 1e3, 3) for r in reps]
     tbs = wl.bytes / (ms * 1e-3) / 1e12
     tflops = wl.flops / (ms * 1e-3) / 1e12
     d["essential_TBps"] = round(tbs, 4)
@@ -325,30 +351,121 @@ def summarize(wl, ms):
     return d
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle on a bounded sample of the headline decode workload: whole
-    sequences, one after another, until about budget_s of wall time is spent."""
+def _oracle_threads():
+    import oracle
+    n = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    oracle.set_num_threads(n)
+    return n
+
+
+def cpu_baseline_of(wl, runs):
+    """The oracle (as it stands) on one named logits workload, in the metric's
+    unit: essential TB/s for decode, fp8-equivalent TFLOP/s for prefill.
+    Whole workloads where that takes seconds (median of `runs` runs); the long
+    prefill chunk on a sample of every 8th query row (its windows, and so its
+    work per row, span the whole causal triangle), one run."""
     import oracle
     from sparse_attention_indexer_scaled_amd import workload
     h = wl.host
-    nthreads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    oracle.set_num_threads(nthreads)
-    done, t0 = [], time.time()
-    for b in range(h.B):
-        oracle.decode(h.q[b:b + 1], h.kv_cache, h.weights[b * h.next_n:(b + 1) * h.next_n],
-                      h.context_lens[b:b + 1], h.block_tables[b:b + 1], h.max_model_len, h.block_size,
-                      preshuffle=h.preshuffle)
-        done.append(b)
-        if time.time() - t0 > budget_s:
-            break
-    dt = time.time() - t0
-    ctx = h.context_lens[done]
-    nbytes = workload.decode_essential_bytes(len(done), h.next_n, ctx, h.max_model_len, H=h.H,
-                                             D=h.D, block_size=h.block_size)
-    return {"value": round(nbytes / dt / 1e12, 8), "unit": "TB/s", "cores": nthreads,
-            "kind": "oracle", "cpu": cpu_model(), "seconds": round(dt, 2),
-            "sample": "%d of %d sequences (all %d rows each, every position to max_model_len) of %s"
-                      % (len(done), h.B, h.next_n, wl.cfg["name"])}
+    nthreads = _oracle_threads()
+    times = []
+    if wl.kind == "prefill":
+        rows = np.arange(h.M) if h.M <= 1024 else np.arange(0, h.M, 8)
+        for _ in range(runs):
+            t0 = time.time()
+            oracle.prefill(h.q[rows], h.k, h.kv_scale, h.weights[rows], h.ks[rows], h.ke[rows])
+            times.append(time.time() - t0)
+        dt = float(np.median(times))
+        flops = workload.prefill_valid_pairs(h.ks[rows], h.ke[rows], h.N) * \
+            workload.flops_per_pair(H=h.H, D=h.D)
+        value, unit = flops / dt / 1e12, "TFLOP/s"
+        sample = ("all %d rows" % h.M if rows.size == h.M else
+                  "%d of %d query rows (every 8th)" % (rows.size, h.M))
+        full_s = dt * wl.pairs / max(workload.prefill_valid_pairs(h.ks[rows], h.ke[rows], h.N), 1)
+    else:
+        for _ in range(runs):
+            t0 = time.time()
+            oracle.decode(h.q, h.kv_cache, h.weights, h.context_lens, h.block_tables,
+                          h.max_model_len, h.block_size, preshuffle=h.preshuffle)
+            times.append(time.time() - t0)
+        dt = float(np.median(times))
+        value, unit = wl.bytes / dt / 1e12, "TB/s"
+        sample = "all %d sequences, %d rows each, every position to max_model_len" % (
+            h.B, h.next_n)
+        full_s = dt
+    return {"value": round(value, 8), "unit": unit, "cores": nthreads, "kind": "oracle",
+            "cpu": cpu_model(), "seconds": round(dt, 3), "runs": runs,
+            "us_per_call_full_workload": round(full_s * 1e6, 1), "sample": "%s of %s" % (
+                sample, wl.cfg["name"])}
+
+
+def load_calib():
+    import ctypes
+    from sparse_attention_indexer_scaled_amd import build
+    if not os.path.exists(build.CALIB_LIB):
+        build.build_calib()
+    lib = ctypes.CDLL(build.CALIB_LIB)
+    lib.mqa_calib_empty.restype = ctypes.c_int
+    lib.mqa_calib_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    lib.mqa_calib_mfma_fp8.restype = ctypes.c_int
+    lib.mqa_calib_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+class EmptyKernel:
+    """The launch floor: one empty kernel per call, timed like a workload."""
+
+    def __init__(self, lib):
+        self.lib = lib
+        self.nsets = 1
+        self.cfg = {"name": "empty_kernel"}
+
+    def call(self, i):
+        import torch
+        rc = self.lib.mqa_calib_empty(1, torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, "empty kernel launch failed"
+
+
+def launch_floor(lib, steps, repeats):
+    """Per-launch microseconds of an empty kernel: replayed from a HIP graph
+    (how the launch-bound workloads are timed) and as back-to-back launches."""
+    wl = EmptyKernel(lib)
+    g_ms, g_reps = time_workload(wl, steps, 4, graph=True, settle_s=0.05, repeats=repeats)
+    e_ms, e_reps = time_workload(wl, steps, 4, graph=False, settle_s=0.05, repeats=repeats)
+    return {"graph_us": round(g_ms * 1e3, 3), "eager_us": round(e_ms * 1e3, 3),
+            "graph_repeats_us": [round(r * 1e3, 3) for r in g_reps],
+            "eager_repeats_us": [round(r * 1e3, 3) for r in e_reps]}
+
+
+MFMA_CALIB_BLOCKS = 1024  # 4 waves each: 16 waves per CU on 256 CUs
+MFMA_CALIB_ITERS = 1024   # 4 MFMAs per iteration and wave
+
+
+def mfma_peak(lib, repeats=5):
+    """fp8 MFMA rate of waves that issue only independent 32x32x64 fp8 MFMAs
+    (131072 flops each), median of `repeats` single-launch timings."""
+    import torch
+    out = torch.empty(MFMA_CALIB_BLOCKS * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    launch = lambda: lib.mqa_calib_mfma_fp8(MFMA_CALIB_BLOCKS, MFMA_CALIB_ITERS, out.data_ptr(),
+                                            stream.cuda_stream)
+    for _ in range(3):
+        assert launch() == 0, "MFMA calibration launch failed"
+    torch.cuda.synchronize()
+    flops = MFMA_CALIB_BLOCKS * 4 * MFMA_CALIB_ITERS * 4 * 131072
+    reps = []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return {"fp8_TFLOPs": round(float(np.median(reps)), 1),
+            "repeats_TFLOPs": [round(r, 1) for r in reps],
+            "kernel": "%d workgroups x 4 waves, each %d independent 32x32x64 fp8 MFMAs" % (
+                MFMA_CALIB_BLOCKS, MFMA_CALIB_ITERS * 4)}
 
 
 def parse_tunables(text):
@@ -464,17 +581,25 @@ def write_kernel_stats(workload_name, stats_dir, command):
     if not paths:
         raise SystemExit("no kernel_stats.csv under %s" % stats_dir)
     rows = list(csv.DictReader(open(paths[0])))
+    # per-dispatch durations from the kernel trace of the same run, for the median
+    durations = {}
+    for tp in glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for t in csv.DictReader(open(tp)):
+            durations.setdefault(t["Kernel_Name"], []).append(
+                int(t["End_Timestamp"]) - int(t["Start_Timestamp"]))
     lines = ["# rocprofv3 kernel statistics: %s" % workload_name,
              "# command: %s" % command,
              "# source_hash: %s" % source_hash(kernel_of(workload_name)),
-             "name | calls | average_ns | min_ns | max_ns | percent"]
+             "name | calls | average_ns | median_ns | min_ns | max_ns | percent"]
     for r in rows:
         # drop the argument list: the first "(" that is not part of
         # "(anonymous namespace)"
         full = r["Name"].replace("(anonymous namespace)", "<anon>")
         name = full.split("(")[0].replace("<anon>", "(anonymous namespace)")
-        lines.append("%s | %s | %.1f | %s | %s | %s" % (name, r["Calls"], float(r["AverageNs"]),
-                                                         r["MinNs"], r["MaxNs"], r["Percentage"]))
+        d = durations.get(r["Name"])
+        med = "%.1f" % float(np.median(d)) if d else "-"
+        lines.append("%s | %s | %.1f | %s | %s | %s | %s" % (
+            name, r["Calls"], float(r["AverageNs"]), med, r["MinNs"], r["MaxNs"], r["Percentage"]))
     os.makedirs(PROFILE_DIR, exist_ok=True)
     path = os.path.join(PROFILE_DIR, "%s_kernel_stats.txt" % workload_name)
     with open(path, "w") as f:
@@ -528,6 +653,10 @@ def write_counter_profile(workload_name, kernel_part, dirs, command):
             derived["mfma_busy_frac"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles, 4)
         if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
             derived["non_mfma_valu_insts"] = int(avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"])
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            # share of the MFMA pipe's busy cycles during which VALU work also ran
+            derived["valu_coexec_frac_of_mfma_busy"] = round(
+                avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
     if "SQ_INSTS_VALU_MFMA_MOPS_F8" in avg:
         # one MOPS unit is 512 flops
         derived["mfma_fp8_flops"] = int(avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512)
@@ -600,25 +729,49 @@ def main():
     if args.calib_copy:
         calib_copy(args.calib_copy)
         return
+    calib = load_calib()
+    if args.calib_mfma:
+        print(json.dumps(mfma_peak(calib)))
+        return
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 4, 3, 0, 5, 6, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21)
-         if i != args.workload]
-    results, head = {}, None
+        [i for i in (1, 22, 4, 3, 0, 5, 6, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20,
+                     21) if i != args.workload]
+    results, head, cpu = {}, None, {}
     for idx in order:
         wl = make_workload(idx, args.hot, tun)
-        ms = time_workload(wl, args.steps, args.warmup, graph=False if args.no_graph else None)
-        results[wl.cfg["name"]] = summarize(wl, ms)
+        ms, reps = time_workload(wl, args.steps, args.warmup,
+                                 graph=False if args.no_graph else None, repeats=args.repeats)
+        res = results[wl.cfg["name"]] = summarize(wl, ms, reps)
+        if not args.hot and idx in HOT_ALSO and wl.nsets > 1:
+            # the same calls on one input copy: what a MALL-resident working set gives
+            cold_sets, wl.nsets = wl.nsets, 1
+            hms, hreps = time_workload(wl, args.steps, 0, graph=wl.graph, settle_s=0.05,
+                                       repeats=args.repeats)
+            wl.nsets = cold_sets
+            res["hot_us_per_call"] = round(hms * 1e3, 3)
+            res["hot_repeats_us"] = [round(r * 1e3, 3) for r in hreps]
+            res["hot_essential_TBps"] = round(wl.bytes / (hms * 1e-3) / 1e12, 4)
         counters = read_counters(wl.cfg["name"])
         if counters:
-            results[wl.cfg["name"]]["counters"] = counters
-        print("[bench] %s: %.2f us/call" % (wl.cfg["name"], ms * 1e3), file=sys.stderr, flush=True)
+            res["counters"] = counters
+        print("[bench] %s: %.2f us/call (repeats %s)" % (
+            wl.cfg["name"], ms * 1e3, " ".join("%.2f" % (r * 1e3) for r in reps)),
+            file=sys.stderr, flush=True)
+        if not args.no_cpu and idx in CPU_BASELINE_RUNS and args.only is None:
+            cpu[wl.cfg["name"]] = cpu_baseline_of(wl, CPU_BASELINE_RUNS[idx])
+            print("[bench] cpu oracle %s: %.2f s" % (wl.cfg["name"], cpu[wl.cfg["name"]]["seconds"]),
+                  file=sys.stderr, flush=True)
         if idx == order[0]:
             head = (wl, ms)
         else:
             del wl
             torch.cuda.empty_cache()
+    floor = launch_floor(calib, args.steps, args.repeats)
+    peak = mfma_peak(calib)
+    print("[bench] launch floor %.2f us (graph) / %.2f us (eager); fp8 MFMA %.0f TFLOP/s" % (
+        floor["graph_us"], floor["eager_us"], peak["fp8_TFLOPs"]), file=sys.stderr, flush=True)
 
     wl, ms = head
     r = results[wl.cfg["name"]]
@@ -658,11 +811,21 @@ def main():
                       "traffic": read_traffic(wl.cfg["name"])} if hbm_bound else
                      {"bound": "mfma", "achieved": r["fp8_TFLOPs"], "peak": FP8_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": r["mfma_frac"],
+                      "peak_measured": peak["fp8_TFLOPs"],
+                      "frac_of_measured": round(r["fp8_TFLOPs"] / peak["fp8_TFLOPs"], 4),
                       "traffic": read_traffic(wl.cfg["name"])}),
+        "calibration": {"launch_floor": floor, "fp8_mfma_measured": peak},
         "workloads": results,
     }
-    if not args.no_cpu and decode:
-        line["cpu_baseline"] = cpu_baseline(wl)
+    for res in results.values():
+        if res["timing"] == "hip graph replay":
+            res["x_launch_floor"] = round(res["us_per_call"] / floor["graph_us"], 3)
+        if "fp8_TFLOPs" in res:
+            res["mfma_frac_of_measured"] = round(res["fp8_TFLOPs"] / peak["fp8_TFLOPs"], 4)
+    if not args.no_cpu and wl.kind in ("decode", "prefill"):
+        line["cpu_baseline"] = cpu.get(wl.cfg["name"]) or cpu_baseline_of(wl, 3)
+        if cpu:
+            line["cpu_baselines"] = cpu
     print(json.dumps(line))
 
 

@@ -24,6 +24,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmqa_indexer.so")
+CALIB_LIB = os.path.join(PKG, "libmqa_calib.so")
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "decode_heads.hip", "decode_d64.hip",
            "decode_fused.hip", "decode_fused_d64.hip", "topk.hip", "kcache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,7 +51,18 @@ def build(resource_usage: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    build_calib()
     return LIB
+
+
+def build_calib() -> str:
+    """The benchmark's calibration kernels (empty launch, MFMA-only loop) in a
+    library of their own, so the op's library holds only the op."""
+    tmp = CALIB_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC] + COMMON + DEVICE + ["-shared", os.path.join(CSRC, "calib.hip"),
+                                                      "-o", tmp])
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
 
 
 if __name__ == "__main__":

@@ -41,12 +41,22 @@ struct PrefillArgs {
 
 
 // Step starting at column n0.  Rows past N are clamped to N - 1: the load stays
-// in bounds and the column is never stored.
-template <int D>
+// in bounds and the column is never stored.  A step that ends at or before N
+// (every step but possibly the last) needs no clamp; that path is only taken
+// at 32 heads (FAST), where it does not cost the kernel a wave per SIMD.
+template <int D, bool FAST>
 __device__ __forceinline__ void load_kstep(KStepOf<D> &k, const uint8_t *kbuf, const float *scale,
                                            int64_t n0, int N, int lane)
 {
     const int t = lane & 31;
+    if (FAST && n0 + kStep <= N) {
+        const uint8_t *p = kbuf + (n0 + t) * D;
+        load_frag(k.t[0], p, lane);
+        load_frag(k.t[1], p + kTile * D, lane);
+        k.sc[0] = scale[n0 + t];
+        k.sc[1] = scale[n0 + kTile + t];
+        return;
+    }
     const int64_t n_a = min(n0 + t, (int64_t)N - 1);
     const int64_t n_b = min(n0 + kTile + t, (int64_t)N - 1);
     load_frag(k.t[0], kbuf + n_a * D, lane);
@@ -80,6 +90,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
 
     int lo[BM], hi[BM];
     int ulo = N, uhi = 0;
+    // Columns inside every row's window: [ilo, ihi) (empty unless the block
+    // has all BM rows and each of them a non-empty window)
+    int ilo = 0, ihi = nrows == BM ? N : 0;
 #pragma unroll
     for (int r = 0; r < BM; ++r) {
         lo[r] = 0;
@@ -91,6 +104,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
                 ulo = min(ulo, lo[r]);
                 uhi = max(uhi, hi[r]);
             }
+            ilo = max(ilo, lo[r]);
+            ihi = min(ihi, hi[r]);
         }
     }
     if (uhi <= ulo) {
@@ -130,7 +145,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
                 load_weights(w[r][ht], wbuf + row * H + ht * kHeads, lane);
             }
         }
+        // this lane's output element relative to row 2i, column 0 of a pair
+        const int laneoff = half * N + t;
         auto store_step = [&](int step, const float (&tot)[2][NP]) {
+            const int n0 = step * kStep;
+            if (HT == 1 && n0 >= ilo && n0 + kStep <= ihi) {
+                // every column of the step is inside every row's window (and
+                // the block has all BM rows; an odd BM's last pair is a single
+                // row whose upper half stores nothing)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < NP; ++i)
+                        if (2 * i + 1 < BM || !half)
+                            (out + (int64_t)(2 * i) * N + n0 + h * kTile)[laneoff] = tot[h][i];
+                return;
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int n = step * kStep + h * kTile + t;
@@ -147,9 +177,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
         // step's loads before waiting for the current one (the
         // sched_barrier keeps the compiler from hoisting the wait above them).
         KStepOf<D> A, B;
-        load_kstep(A, kbuf, scale, (int64_t)st * kStep, N, lane);
+        load_kstep<D, HT == 1>(A, kbuf, scale, (int64_t)st * kStep, N, lane);
         while (true) {
-            load_kstep(B, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
+            load_kstep<D, HT == 1>(B, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
             __builtin_amdgcn_sched_barrier(0);
             float tot[2][NP];
             step_scores<BM, HT, D>(A, q, w, tot);
@@ -157,7 +187,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t *__restrict_
             st += nw;
             if (st >= st1)
                 break;
-            load_kstep(A, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
+            load_kstep<D, HT == 1>(A, kbuf, scale, (int64_t)min(st + nw, st1 - 1) * kStep, N, lane);
             __builtin_amdgcn_sched_barrier(0);
             step_scores<BM, HT, D>(B, q, w, tot);
             store_step(st, tot);

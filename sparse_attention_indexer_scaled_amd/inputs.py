@@ -342,6 +342,10 @@ CONFIGS = {
     # the headline decode shape at head dim 64 (64-byte K rows)
     21: dict(kind="decode", name="decode_B16_nn6_ctx131072_d64", B=16, next_n=6, ctx=131072,
              mml=131072, D=64),
+    # the long-context decode at next_n 1: the read stream with the least
+    # compute per byte (the shape of the issue page's ~5.4 TB/s figure)
+    22: dict(kind="decode", name="decode_B16_nn1_ctx131072", B=16, next_n=1, ctx=131072,
+             mml=131072),
 }
 
 

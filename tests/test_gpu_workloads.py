@@ -54,14 +54,17 @@ def test_prefill_workload(idx):
     assert not np.isnan(out).any(), "unwritten output positions"
     assert np.array_equal(np.isneginf(out), ~win)
     assert np.isfinite(out[win]).all()
-    rows = np.arange(p.M) if p.M <= 64 else np.array([0, 1, 2, 3, 1000, 2047, 3001, 4092, 4093, 4094, 4095])
+    # every row of the small chunk; on the long chunks every 16th row plus the
+    # first and last rows (the shortest and longest windows)
+    rows = np.arange(p.M) if p.M <= 64 else np.unique(np.concatenate(
+        [np.arange(0, p.M, 16), [1, 2, 3, 1000, 2047, 3001, p.M - 4, p.M - 3, p.M - 2, p.M - 1]]))
     t0 = time.time()
     ref, mag = oracle_prefill(p, rows)
     say("oracle rows %s: %.1fs" % (len(rows), time.time() - t0))
     assert_parity(out[rows], ref, mag, f"workload{idx}")
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20, 21])
+@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20, 21, 22])
 def test_decode_workload(idx):
     t0 = time.time()
     d = inputs.make_config(idx, poison=True)
@@ -75,7 +78,7 @@ def test_decode_workload(idx):
     if idx == 4:
         seqs = [int(np.argmin(d.context_lens)), int(np.argmax(d.context_lens)), 17]
     elif idx == 2:
-        seqs = [9]
+        seqs = list(range(d.B))  # the headline: every row
     else:
         seqs = [0, 15]
     t0 = time.time()
