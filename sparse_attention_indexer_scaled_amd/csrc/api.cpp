@@ -352,7 +352,8 @@ extern "C" int paged_mqa_logits_decode(const uint8_t *q_fp8, const uint8_t *kv_c
 
 extern "C" size_t paged_mqa_topk_workspace_size(int batch, int next_n, int max_model_len)
 {
-    if (batch <= 0 || next_n < 1 || next_n > 8 || max_model_len <= 0)
+    if (batch <= 0 || next_n < 1 || next_n > 8 || max_model_len <= 0 ||
+        (int64_t)batch * next_n > INT32_MAX)
         return 0;
     return mqa::fused_workspace(nullptr, batch * next_n, max_model_len).bytes;
 }
