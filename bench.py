@@ -609,6 +609,7 @@ def write_kernel_stats(workload_name, stats_dir, command):
 
 NUM_SIMDS = 256 * 4   # MI355X: 256 CUs x 4 SIMDs
 NUM_XCDS = 8          # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+GUI_MIN_DISPATCH_US = 20
 
 
 def _pmc_dispatches(csv_dir, name_part):
@@ -646,6 +647,12 @@ def write_counter_profile(workload_name, kernel_part, dirs, command):
            "command": command}
     derived = {}
     gui = avg.get("GRBM_GUI_ACTIVE")
+    if gui and out["median_dispatch_us"] < GUI_MIN_DISPATCH_US:
+        # the counter window of a dispatch this short is longer than the
+        # dispatch itself, so per-cycle figures would be diluted by idle time
+        derived["note"] = ("dispatch under %d us: clock and pipe-busy fractions omitted"
+                           % GUI_MIN_DISPATCH_US)
+        gui = None
     if gui:
         simd_cycles = NUM_SIMDS * gui / NUM_XCDS
         derived["clock_GHz"] = round(gui / NUM_XCDS / (out["median_dispatch_us"] * 1e3), 3)

@@ -296,7 +296,12 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     //   split: at least ~1024 workgroups, and at most 32 steps (2048 tokens)
     //          per workgroup at the longest context, but at least 2 steps;
     //          more workgroups per sequence than that measured slower (longer
-    //          prologues relative to the work, more concurrent streams).
+    //          prologues relative to the work, more concurrent streams).  At
+    //          128 heads a wave holds one row (~218 VGPRs, 2 waves per SIMD), so
+    //          one next_n-wave workgroup fills a CU: there the target is ~256
+    //          workgroups and at most 128 steps each (B 16, 131072 tokens,
+    //          next_n 6, one GPU: split 16 210.8 us, 32 212.6 us; the 1024-
+    //          workgroup rule's 64: 220-226 us).
     const int rows_default = next_n == 4 ? 1 : next_n > 4 ? 2 : (next_n + 1) / 2;
     int rows = t.rows_per_block ? t.rows_per_block : rows_default;
     rows = std::min(std::min(rows, next_n), max_rows);
@@ -313,8 +318,11 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
     if (t.split_kv) {
         p.split_kv = t.split_kv;
     } else {
-        const int64_t want = short_ctx ? steps_max
-                                       : std::max(ceil_div(1024, batch), ceil_div(steps_max, 32));
+        const bool one_wg_per_cu = head_tiles == 4;
+        const int64_t want =
+            short_ctx ? steps_max
+                      : one_wg_per_cu ? std::max(ceil_div(256, batch), ceil_div(steps_max, 128))
+                                      : std::max(ceil_div(1024, batch), ceil_div(steps_max, 32));
         const int64_t cap = std::max<int64_t>(1, short_ctx ? steps_max : steps_max / 2);
         p.split_kv = (int)std::max<int64_t>(1, std::min(want, cap));
     }
