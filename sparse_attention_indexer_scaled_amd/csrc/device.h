@@ -92,19 +92,18 @@ __device__ __forceinline__ f32x16 row_scores(const Operand<D> &q, const Operand<
     return acc;
 }
 
-// sum over this lane's 16 heads of relu(S) * w.  Built with -fno-honor-nans, so
-// each relu is a single v_max_f32 (no IEEE canonicalize first).
+// sum over this lane's 16 heads of relu(S) * w, in register order: one max
+// and one FMA per head (the first a multiply), in a single chain, since the
+// items of a step give the scheduler independent chains enough.  Built with
+// -fno-honor-nans, so each relu is a single v_max_f32 (no IEEE canonicalize
+// first).
 __device__ __forceinline__ float relu_weight_sum(const f32x16 &s, const Weights16 &w)
 {
-    float a = 0.f, b = 0.f;
+    float a = fmaxf(s[0], 0.f) * w.c[0][0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        a = fmaf(fmaxf(s[4 * q + 0], 0.f), w.c[q][0], a);
-        b = fmaf(fmaxf(s[4 * q + 1], 0.f), w.c[q][1], b);
-        a = fmaf(fmaxf(s[4 * q + 2], 0.f), w.c[q][2], a);
-        b = fmaf(fmaxf(s[4 * q + 3], 0.f), w.c[q][3], b);
-    }
-    return a + b;
+    for (int r = 1; r < 16; ++r)
+        a = fmaf(fmaxf(s[r], 0.f), w.c[r / 4][r % 4], a);
+    return a;
 }
 
 // Finish the head sum of two rows at once.  v_permlane32_swap exchanges the

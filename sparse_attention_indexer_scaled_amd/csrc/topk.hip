@@ -488,22 +488,17 @@ __device__ __forceinline__ void append4(TopkShared &sh, float4 v, int c, bool k0
     append(sh, k3, entry(order_key(v.w), c + 3), lane);
 }
 
-// First batch of the filter pass on a 16-byte aligned row (columns 4 (tid +
-// u kThreads) .. +3), loaded before the threshold is known so that its
-// latency overlaps the sampling.
-__device__ __forceinline__ void load_batch(const float *x, int cols, int b, float4 (&v)[kUnroll])
+// One batch of the filter pass on a 16-byte aligned row: groups b + u kThreads
+// (columns 4 i .. 4 i + 3), u < kUnroll.  Groups past the row end (i >= n4 =
+// cols / 4 >= 1) read the last group again, and the caller drops them by
+// index: nothing here consumes the loads, so the first batch, requested
+// before the sampling, is only waited for by the filter pass.
+__device__ __forceinline__ void load_batch(const float *x, int n4, int b, float4 (&v)[kUnroll])
 {
-    const float ninf = -__builtin_inff();
-    const float4 pad = make_float4(ninf, ninf, ninf, ninf);
-    const int n4 = cols >> 2;
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        // unconditional in-bounds load (index clamped), then select, so the
-        // compiler keeps one 16-byte load per element
-        const int i = b + u * kThreads;
-        v[u] = select4(i < n4, x4[min(i, n4 - 1)], pad);
-    }
+    for (int u = 0; u < kUnroll; ++u)
+        v[u] = x4[min(b + u * kThreads, n4 - 1)];
 }
 
 // Append every entry >= f0 (a finite value) to sh.buf, counting them all in
@@ -511,16 +506,20 @@ __device__ __forceinline__ void load_batch(const float *x, int cols, int b, floa
 // LDS atomic for all of their survivors: lane offsets come from the ballots
 // of the four components, so no lane exchange is needed.  On an aligned row
 // `first` holds the thread's first batch (load_batch at b = tid).
+template <bool ALIGNED>
 __device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, int tid, int lane,
                             const float4 (&first)[kUnroll])
 {
     const uint64_t lt = (1ull << lane) - 1ull;
-    auto emit = [&](const float4 (&v)[kUnroll], const int (&col)[kUnroll]) {
+    auto emit = [&](const float4 (&v)[kUnroll], const int (&col)[kUnroll],
+                    const bool (&ok)[kUnroll]) {
         int total = 0;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            total += __popcll(__ballot(v[u].x >= f0)) + __popcll(__ballot(v[u].y >= f0)) +
-                     __popcll(__ballot(v[u].z >= f0)) + __popcll(__ballot(v[u].w >= f0));
+            total += __popcll(__ballot(ok[u] && v[u].x >= f0)) +
+                     __popcll(__ballot(ok[u] && v[u].y >= f0)) +
+                     __popcll(__ballot(ok[u] && v[u].z >= f0)) +
+                     __popcll(__ballot(ok[u] && v[u].w >= f0));
         if (total == 0)
             return;
         const uint64_t active = __ballot(1);
@@ -528,26 +527,24 @@ __device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, 
         if (lane == __ffsll((unsigned long long)active) - 1)
             base = atomicAdd(&sh.count, total);
         base = __builtin_amdgcn_readfirstlane(base);
-        auto put = [&](float f, int c) {
-            const uint64_t b = __ballot(f >= f0);
-            if (f >= f0 && base + __popcll(b & lt) < kSortCap)
+        auto put = [&](bool keep, float f, int c) {
+            const uint64_t b = __ballot(keep);
+            if (keep && base + __popcll(b & lt) < kSortCap)
                 sh.buf[base + __popcll(b & lt)] = entry(order_key(f), c);
             base += __popcll(b);
         };
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            put(v[u].x, col[u]);
-            put(v[u].y, col[u] + 1);
-            put(v[u].z, col[u] + 2);
-            put(v[u].w, col[u] + 3);
+            put(ok[u] && v[u].x >= f0, v[u].x, col[u]);
+            put(ok[u] && v[u].y >= f0, v[u].y, col[u] + 1);
+            put(ok[u] && v[u].z >= f0, v[u].z, col[u] + 2);
+            put(ok[u] && v[u].w >= f0, v[u].w, col[u] + 3);
         }
     };
-    const float ninf = -__builtin_inff();
-    const float4 pad = make_float4(ninf, ninf, ninf, ninf);
     float4 v[kUnroll];
     int col[kUnroll];
-    int i0 = 0;
-    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    bool ok[kUnroll];
+    if constexpr (ALIGNED) {
         const int n4 = cols >> 2;
         for (int b = tid; b < n4; b += kUnroll * kThreads) {
             if (b == tid) {
@@ -555,20 +552,25 @@ __device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, 
                 for (int u = 0; u < kUnroll; ++u)
                     v[u] = first[u];
             } else {
-                load_batch(x, cols, b, v);
+                load_batch(x, n4, b, v);
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < kUnroll; ++u) {
                 col[u] = 4 * (b + u * kThreads);
-            emit(v, col);
+                ok[u] = b + u * kThreads < n4;
+            }
+            emit(v, col, ok);
         }
-        i0 = 4 * n4;
+        if ((cols & 3) == 0)
+            return;
     }
+    const float ninf = -__builtin_inff();
+    const int i0 = ALIGNED ? cols & ~3 : 0;
     for (int b = i0 + 4 * tid; b < cols; b += 4 * kUnroll * kThreads) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int i = b + 4 * u * kThreads;
-            v[u] = pad;
+            v[u] = make_float4(ninf, ninf, ninf, ninf);
             if (i < cols)
                 v[u].x = x[i];
             if (i + 1 < cols)
@@ -578,20 +580,31 @@ __device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, 
             if (i + 3 < cols)
                 v[u].w = x[i + 3];
             col[u] = i;
+            ok[u] = true;
         }
-        emit(v, col);
+        emit(v, col, ok);
     }
 }
 
 // The 24-bit prefix of the ts-th largest of the keys the block holds
 // (EPT per thread; 0 = not listable), located by two 12-bit histograms; 0
 // when fewer than ts keys are listable.
+// Zero the 4096 bins, as straight-line code (a loop here would make the
+// compiler drain every outstanding load at its head).
+template <int NT, class SH>
+__device__ __forceinline__ void clear_hist(SH &sh, int tid)
+{
+    static_assert(kMaxBins % NT == 0, "whole rounds of the block");
+#pragma unroll
+    for (int r = 0; r < kMaxBins / NT; ++r)
+        sh.hist[tid + r * NT] = 0;
+}
+
 template <int NT, int EPT, class SH>
 __device__ __forceinline__ uint32_t keys_threshold(SH &sh, const uint32_t (&samp)[EPT], int ts,
                                                    int tid, int lane, int wave)
 {
-    for (int i = tid; i < kMaxBins; i += NT)
-        sh.hist[i] = 0;
+    clear_hist<NT>(sh, tid);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < EPT; ++s)
@@ -606,8 +619,7 @@ __device__ __forceinline__ uint32_t keys_threshold(SH &sh, const uint32_t (&samp
     const uint32_t b0 = (uint32_t)sh.bcast[0];
     const int above0 = sh.bcast[1];
     __syncthreads();  // hist and bcast are reused below
-    for (int i = tid; i < kMaxBins; i += NT)
-        sh.hist[i] = 0;
+    clear_hist<NT>(sh, tid);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < EPT; ++s)
@@ -634,31 +646,73 @@ __device__ __forceinline__ int sample_rank(float m)
 // adjacent columns, evenly spaced), about 1.25 k entries plus a few standard
 // deviations are >= t0.  0 when the sample holds too few listable keys.
 // Needs cols > kSample.
-template <int NT, class SH>
-__device__ __forceinline__ uint32_t sample_threshold(SH &sh, const float *x, int cols, int k, int tid,
-                                                     int lane, int wave)
-{
-    // sample entries g = EPT tid .. EPT tid + EPT - 1: run g / 16, offset g % 16
-    constexpr int EPT = kSample / NT;
+// The threshold sample: entries g = EPT tid .. EPT tid + EPT - 1 of kSample,
+// entry g at run g / 16, offset g % 16 of 256 evenly spaced 16-column runs.
+template <int NT>
+struct RowSample {
+    static constexpr int EPT = kSample / NT;
     static_assert(EPT % 4 == 0 && 16 % EPT == 0, "whole float4 groups inside one run");
+    float4 f[EPT / 4];
+};
+
+template <int NT, bool ALIGNED>
+__device__ __forceinline__ void sample_load(RowSample<NT> &rs, const float *x, int cols, int tid)
+{
+    constexpr int EPT = RowSample<NT>::EPT;
     const int g = EPT * tid;
     const int pos = (int)(((int64_t)(g / 16) * cols / 256) & ~(int64_t)15) + g % 16;
-    uint32_t samp[EPT];
 #pragma unroll
     for (int j = 0; j < EPT / 4; ++j) {
         const int q = pos + 4 * j;
-        float4 f;
-        if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
-            f = *reinterpret_cast<const float4 *>(x + q);
+        if constexpr (ALIGNED)
+            rs.f[j] = *reinterpret_cast<const float4 *>(x + q);
         else
-            f = make_float4(x[q], x[q + 1], x[q + 2], x[q + 3]);
-        samp[4 * j + 0] = order_key(f.x);
-        samp[4 * j + 1] = order_key(f.y);
-        samp[4 * j + 2] = order_key(f.z);
-        samp[4 * j + 3] = order_key(f.w);
+            rs.f[j] = make_float4(x[q], x[q + 1], x[q + 2], x[q + 3]);
+    }
+}
+
+// A threshold key aimed at ~1.25 k survivors of the row (0: none).
+template <int NT, class SH>
+__device__ __forceinline__ uint32_t sample_threshold(SH &sh, const RowSample<NT> &rs, int cols,
+                                                     int k, int tid, int lane, int wave)
+{
+    constexpr int EPT = RowSample<NT>::EPT;
+    uint32_t samp[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+        samp[4 * j + 0] = order_key(rs.f[j].x);
+        samp[4 * j + 1] = order_key(rs.f[j].y);
+        samp[4 * j + 2] = order_key(rs.f[j].z);
+        samp[4 * j + 3] = order_key(rs.f[j].w);
     }
     const int ts = sample_rank((float)kSample * (float)k / (float)cols);
     return keys_threshold<NT, EPT>(sh, samp, ts, tid, lane, wave);
+}
+
+// A long row: the sampled threshold and one filter pass.  Returns the number
+// of survivors when they hold the row's top k (between k and kSortCap), else
+// -1.  On a 16-byte aligned row the first batch of the pass is requested right
+// behind the sample, so its latency overlaps the sampling.
+template <bool ALIGNED>
+__device__ __forceinline__ int filter_row(TopkShared &sh, const float *x, int cols, int k, int tid,
+                                          int lane, int wave)
+{
+    RowSample<kThreads> rs;
+    sample_load<kThreads, ALIGNED>(rs, x, cols, tid);
+    float4 first[kUnroll];
+    if constexpr (ALIGNED)
+        load_batch(x, cols >> 2, tid, first);
+    const uint32_t t0 = sample_threshold(sh, rs, cols, k, tid, lane, wave);
+    if (t0 == 0u)
+        return -1;
+    // order_key(v) >= t0  <=>  v >= f0 (t0 raised to the smallest listable
+    // key changes nothing and keeps f0 finite, so -inf and NaN never pass)
+    const float f0 = key_value(max(t0, 0x00800000u));
+    filter_pass<ALIGNED>(sh, x, cols, f0, tid, lane, first);
+    __syncthreads();
+    const int c = sh.count;
+    __syncthreads();
+    return c >= k && c <= kSortCap ? c : -1;
 }
 
 // Exact selection by radix passes (the path for any row the sampled
@@ -806,22 +860,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
         __syncthreads();
         n = sh.count;
     } else {
-        float4 first[kUnroll];
-        if ((reinterpret_cast<uintptr_t>(x) & 15) == 0)
-            load_batch(x, cols, tid, first);
-        const uint32_t t0 = sample_threshold<kThreads>(sh, x, cols, k, tid, lane, wave);
-        if (t0 != 0u) {
-            // order_key(v) >= t0  <=>  v >= f0 (t0 raised to the smallest
-            // listable key changes nothing and keeps f0 finite, so -inf and
-            // NaN never pass)
-            const float f0 = key_value(max(t0, 0x00800000u));
-            filter_pass(sh, x, cols, f0, tid, lane, first);
-            __syncthreads();
-            const int c = sh.count;
-            if (c >= k && c <= kSortCap)
-                n = c;
-            __syncthreads();
-        }
+        n = (reinterpret_cast<uintptr_t>(x) & 15) == 0 ? filter_row<true>(sh, x, cols, k, tid, lane, wave)
+                                                         : filter_row<false>(sh, x, cols, k, tid, lane, wave);
         if (n < 0)
             n = radix_select(sh, x, cols, k, tid, lane, wave);
     }
@@ -870,7 +910,7 @@ struct ThresholdShared {
     int listable;
 };
 
-constexpr int kThresholdThreads = kThreads;
+constexpr int kThresholdThreads = 256;  // 4 waves: 16 sample keys each thread, fewer waves per barrier
 
 __global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
     const float *__restrict__ sample, const int32_t *__restrict__ ctx_lens, int next_n, int mml,
