@@ -499,6 +499,10 @@ KERNEL_SOURCES = {
                       "decode.hip"),
     "prefill_kernel": ("device.h", "launch.h", "api.cpp", "prefill.hip"),
     "topk_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "topk.hip"),
+    # the fused decode top-k: the decode template's sample and filter modes,
+    # then the threshold and select kernels
+    "fused_topk": ("device.h", "launch.h", "order_key.h", "api.cpp", "decode_kernel.h",
+                   "decode_fused.hip", "topk.hip"),
     "kcache_insert_kernel": ("device.h", "launch.h", "api.cpp", "kcache.hip"),
 }
 
@@ -527,6 +531,8 @@ def source_hash(kernel):
 
 
 def kernel_of(workload_name):
+    if workload_name.startswith("decode_topk"):
+        return "fused_topk"
     for prefix in ("decode", "prefill", "topk", "kcache_insert"):
         if workload_name.startswith(prefix):
             return prefix + "_kernel"

@@ -255,8 +255,9 @@ __device__ void sort_desc(TopkShared &sh, int n2, int tid, int lane)
     __syncthreads();
 }
 
-// Bucket sort of sh.buf[0, n), descending, result in sh.buf (sh.sorted is
-// the scratch).  Keys are spread over kMaxBins buckets linearly in the
+// Bucket sort of sh.buf[0, n), descending; positions [0, min(n, k)) of the
+// result are in sh.buf (sh.sorted is the scratch), and buckets that start at
+// or past position k, whose entries are never output, are left unranked.  Keys are spread over kMaxBins buckets linearly in the
 // value, bucket 0 holding the largest; a prefix sum places the buckets and
 // the entries are scattered to them.  Then every entry of a bucket of up to
 // kBucketMax entries finds its place by itself: the number of entries of its
@@ -268,7 +269,8 @@ __device__ void sort_desc(TopkShared &sh, int n2, int tid, int lane)
 // a bitonic sort is n log^2 n.  Returns false, with sh.buf unchanged, when
 // some bucket holds more than kCrowdMax entries; the caller then sorts
 // sh.buf itself.
-__device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int lane, int wave)
+__device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int k, int tid, int lane,
+                                            int wave)
 {
     if (tid == 0) {
         sh.kmin = 0xffffffffu;
@@ -366,8 +368,8 @@ __device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int 
         const int b = bucket_of(e);
         const int end = (int)sh.hist[b];
         const int st = b > 0 ? (int)sh.hist[b - 1] : 0;
-        if (end - st > kBucketMax)
-            continue;  // ranked below by the whole block
+        if (end - st > kBucketMax || st >= k)
+            continue;  // ranked below by the whole block, or past the output
         // eight reads in flight per round (a dependent read per entry would
         // wait out the LDS latency each time)
         int r = 0;
@@ -386,6 +388,8 @@ __device__ __forceinline__ bool bucket_sort(TopkShared &sh, int n, int tid, int 
     const int ncrowd = sh.ncrowd;
     for (int cb = 0; cb < ncrowd; ++cb) {
         const int st = sh.crowd_start[cb], m = sh.crowd_m[cb];
+        if (st >= k)
+            continue;  // uniform: past the output
         const uint64_t e0 = tid < m ? sh.sorted[st + tid] : 0ull;
         const uint64_t e1 = tid + kThreads < m ? sh.sorted[st + tid + kThreads] : 0ull;
         int r0 = 0, r1 = 0;
@@ -586,9 +590,6 @@ __device__ void filter_pass(TopkShared &sh, const float *x, int cols, float f0, 
     }
 }
 
-// The 24-bit prefix of the ts-th largest of the keys the block holds
-// (EPT per thread; 0 = not listable), located by two 12-bit histograms; 0
-// when fewer than ts keys are listable.
 // Zero the 4096 bins, as straight-line code (a loop here would make the
 // compiler drain every outstanding load at its head).
 template <int NT, class SH>
@@ -600,6 +601,9 @@ __device__ __forceinline__ void clear_hist(SH &sh, int tid)
         sh.hist[tid + r * NT] = 0;
 }
 
+// The 24-bit prefix of the ts-th largest of the keys the block holds
+// (EPT per thread; 0 = not listable), located by two 12-bit histograms; 0
+// when fewer than ts keys are listable.
 template <int NT, int EPT, class SH>
 __device__ __forceinline__ uint32_t keys_threshold(SH &sh, const uint32_t (&samp)[EPT], int ts,
                                                    int tid, int lane, int wave)
@@ -642,10 +646,6 @@ __device__ __forceinline__ int sample_rank(float m)
     return (int)ceilf(1.25f * m + 3.0f * sqrtf(m) + 4.0f);
 }
 
-// A key t0 such that, judging by kSample entries of the row (256 runs of 16
-// adjacent columns, evenly spaced), about 1.25 k entries plus a few standard
-// deviations are >= t0.  0 when the sample holds too few listable keys.
-// Needs cols > kSample.
 // The threshold sample: entries g = EPT tid .. EPT tid + EPT - 1 of kSample,
 // entry g at run g / 16, offset g % 16 of 256 evenly spaced 16-column runs.
 template <int NT>
@@ -671,7 +671,9 @@ __device__ __forceinline__ void sample_load(RowSample<NT> &rs, const float *x, i
     }
 }
 
-// A threshold key aimed at ~1.25 k survivors of the row (0: none).
+// A key t0 such that, judging by the row's sample, about 1.25 k entries plus a
+// few standard deviations are >= t0.  0 when the sample holds too few listable
+// keys.  Needs cols > kSample.
 template <int NT, class SH>
 __device__ __forceinline__ uint32_t sample_threshold(SH &sh, const RowSample<NT> &rs, int cols,
                                                      int k, int tid, int lane, int wave)
@@ -817,7 +819,7 @@ __device__ int radix_select(TopkShared &sh, const float *x, int cols, int k, int
 __device__ __forceinline__ void sort_and_write(TopkShared &sh, int n, int32_t *out, int k, int tid,
                                                int lane, int wave)
 {
-    if (!bucket_sort(sh, n, tid, lane, wave)) {
+    if (!bucket_sort(sh, n, k, tid, lane, wave)) {
         // Many equal or clustered keys: bitonic sort of the smallest power of
         // two >= n, padded with 0 (ranks last).
         int n2 = 1;
