@@ -123,3 +123,30 @@ def test_zero_columns_writes_minus_one():
 
 def test_zero_rows_is_a_no_op():
     _native.topk_indices(torch.empty((0, 10), dtype=torch.float32, device="cuda"), 4)
+
+
+def _bucketed_row(cols, rng):
+    """A row whose sorted order has, from the top: 60 distinct large values,
+    200 copies of 0.5 (one crowded bucket), 20 values within 1e-6 of 0.25 (one
+    small bucket), then distinct small values; positions shuffled."""
+    top = 50.0 + rng.permutation(60).astype(np.float32)
+    crowd = np.full(200, 0.5, np.float32)
+    near = (0.25 + 1e-6 * rng.random(20)).astype(np.float32)
+    rest = (0.2 * rng.random(cols - 280)).astype(np.float32)
+    row = np.concatenate([top, crowd, near, rest])
+    return row[rng.permutation(cols)]
+
+
+@pytest.mark.parametrize("k", [30, 59, 60, 61, 100, 259, 260, 261, 270, 280, 281, 512])
+def test_sort_buckets_around_k(k):
+    # The sort leaves unranked the buckets that start at or past position k;
+    # k here falls before, at, inside and after the crowded bucket (positions
+    # 60..259) and the small one (260..279).  Short rows (every listable entry
+    # gathered) and a long row (the sampled threshold) both run the sort.
+    rng = np.random.default_rng(4000 + k)
+    say("topk buckets around k=%d" % k)
+    for cols in (4000, 8192):
+        x = np.stack([_bucketed_row(cols, rng) for _ in range(2)])
+        check(x, k, "short rows cols=%d k=%d" % (cols, k))
+    long = _bucketed_row(131072, rng)[None, :]
+    check(long, k, "long row k=%d" % k)
