@@ -97,32 +97,49 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v;
 }
 
-// Wave 0 finds the digit b such that  above + #(digits > b) < k <= above +
-// #(digits >= b),  scanning nbins digits from the top: lane l first sums
-// digits [nbins - (l+1) w, nbins - l w) with w = nbins / 64, a scan finds the
-// lane whose span holds b, and the wave then scans that span one digit per
-// lane.  Writes b, the new `above` and the bucket size to sh.bcast[0..2] (not
-// written when above + total < k), and the total to bcast[3].
-template <class SH>
-__device__ void find_threshold(SH &sh, int nbins, int above, int k, int lane)
+// The block finds the digit b such that  above + #(digits > b) < k <= above +
+// #(digits >= b),  scanning nbins digits from the top: thread t first sums
+// digits [nbins - (t+1) w, nbins - t w) with w = nbins / min(nbins, NT) (every
+// thread of the block at once), a block scan finds the thread whose span holds
+// b, and that thread's wave then scans the span one digit per lane.  Writes b,
+// the new `above` and the bucket size to sh.bcast[0..2] (not written when
+// above + total < k), and the total to bcast[3].  Every thread of the block
+// calls it (it holds a barrier); the caller syncs before reading bcast.
+template <int NT, class SH>
+__device__ __forceinline__ void find_threshold(SH &sh, int nbins, int above, int k, int tid)
 {
-    const int w = nbins / 64;
-    const int hi = nbins - lane * w;  // exclusive upper digit of this lane's span
+    constexpr int NW = NT / 64;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int owners = min(nbins, NT);  // threads that own a span (powers of two)
+    const int w = nbins / owners;
+    const bool owner = tid < owners;
+    const int hi = nbins - tid * w;  // exclusive upper digit of this thread's span
     int mine = 0;
-    // lane l starts its span at offset l: at each step the 64 lanes read 64
-    // different banks (in span order they would all hit one bank)
-    for (int j = 0; j < w; ++j)
-        mine += (int)sh.hist[hi - w + ((j + lane) & (w - 1))];
-    const int incl = wave_inclusive_scan(mine, lane);
-    const int excl = incl - mine;
+    // lane l starts its span at offset l: neighbouring lanes read different banks
+    if (owner)
+        for (int j = 0; j < w; ++j)
+            mine += (int)sh.hist[hi - w + ((j + lane) & (w - 1))];
+    const int incl_w = wave_inclusive_scan(mine, lane);
     if (lane == 63)
-        sh.bcast[3] = incl;
-    const uint64_t hit = __ballot(above + excl < k && above + incl >= k);
+        sh.wave_total[wave] = incl_w;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const int c = sh.wave_total[v];
+        before += v < wave ? c : 0;
+        total += c;
+    }
+    const int incl = before + incl_w;
+    const int excl = incl - mine;
+    if (tid == 0)
+        sh.bcast[3] = total;
+    const uint64_t hit = __ballot(owner && above + excl < k && above + incl >= k);
     if (hit == 0ull)
         return;
-    const int span = __ffsll((unsigned long long)hit) - 1;
+    const int span = __ffsll((unsigned long long)hit) - 1;  // lane of this wave
     const int base = above + __shfl(excl, span, 64);
-    const int d = nbins - span * w - 1 - lane;  // lane j looks at the j-th digit from the top
+    const int d = nbins - (wave * 64 + span) * w - 1 - lane;  // lane j: the j-th digit from the top
     const int c = lane < w ? (int)sh.hist[d] : 0;
     const int run = base + wave_inclusive_scan(c, lane);  // keys with digit >= d
     const uint64_t reach = __ballot(lane < w && run >= k);
@@ -133,9 +150,6 @@ __device__ void find_threshold(SH &sh, int nbins, int above, int k, int lane)
     }
 }
 
-// v from lane (lane ^ M) of the wave: DPP quad permutes for M = 1 and 2,
-// ds_swizzle (bit-mask mode, no LDS access) for 4..16, v_permlane32_swap for
-// 32.
 template <int M>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane)
 {
@@ -615,8 +629,7 @@ __device__ __forceinline__ uint32_t keys_threshold(SH &sh, const uint32_t (&samp
         if (samp[s] != 0u)
             atomicAdd(&sh.hist[samp[s] >> 20], 1u);
     __syncthreads();
-    if (wave == 0)
-        find_threshold(sh, kMaxBins, 0, ts, lane);
+    find_threshold<NT>(sh, kMaxBins, 0, ts, tid);
     __syncthreads();
     if (sh.bcast[3] < ts)
         return 0u;
@@ -630,8 +643,7 @@ __device__ __forceinline__ uint32_t keys_threshold(SH &sh, const uint32_t (&samp
         if (samp[s] != 0u && (samp[s] >> 20) == b0)
             atomicAdd(&sh.hist[(samp[s] >> 8) & 0xfffu], 1u);
     __syncthreads();
-    if (wave == 0)
-        find_threshold(sh, kMaxBins, above0, ts, lane);
+    find_threshold<NT>(sh, kMaxBins, above0, ts, tid);
     __syncthreads();
     const uint32_t t0 = (b0 << 20) | ((uint32_t)sh.bcast[0] << 8);
     __syncthreads();
@@ -750,8 +762,7 @@ __device__ int radix_select(TopkShared &sh, const float *x, int cols, int k, int
             count(v.w);
         });
         __syncthreads();
-        if (wave == 0)
-            find_threshold(sh, nbins, above, k, lane);
+        find_threshold<kThreads>(sh, nbins, above, k, tid);
         __syncthreads();
         if (pass == 0 && sh.bcast[3] <= k) {
             take_all = true;  // at most k listable entries in the row
@@ -906,13 +917,15 @@ struct FusedRowArgs {
     int block_size;  // tokens per cache block: 1, 16, 64 or 128
 };
 
+constexpr int kThresholdThreads = 256;  // 4 waves: 16 sample keys each thread, fewer waves per barrier
+
 struct ThresholdShared {
     uint32_t hist[kMaxBins];
     int bcast[4];
     int listable;
+    int wave_total[kThresholdThreads / 64];
 };
 
-constexpr int kThresholdThreads = 256;  // 4 waves: 16 sample keys each thread, fewer waves per barrier
 
 __global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
     const float *__restrict__ sample, const int32_t *__restrict__ ctx_lens, int next_n, int mml,
