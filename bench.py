@@ -95,6 +95,9 @@ def cpu_model():
 # Top-k workloads: index -> (decode workload whose logits are ranked, k).  The
 # pages' deployments use index_topk 2048 and 512.
 TOPK_WORKLOADS = {5: (2, 2048), 6: (2, 512)}
+# The same top-k through mqa_topk_indices_ws (each long row split over several
+# workgroups, with a workspace allocated once): index -> (decode workload, k).
+TOPK_WS_WORKLOADS = {23: (2, 2048), 24: (2, 512)}
 # K-cache insert workloads: index -> (tokens, bf16 input).  4096 tokens is the
 # long prefill chunk's K; 96 is one decode step of the MTP workload (16 x 6).
 KCACHE_WORKLOADS = {7: (4096, False), 8: (96, True)}
@@ -169,7 +172,8 @@ class TopkWorkload:
 
     def __init__(self, idx, hot):
         import torch
-        decode_idx, k = TOPK_WORKLOADS[idx]
+        self.split = idx in TOPK_WS_WORKLOADS
+        decode_idx, k = (TOPK_WS_WORKLOADS if self.split else TOPK_WORKLOADS)[idx]
         src = Workload(decode_idx, True)
         src.call(0)
         torch.cuda.synchronize()
@@ -178,7 +182,8 @@ class TopkWorkload:
         self.idx = idx
         self.kind = "topk"
         self.k = k
-        self.cfg = {"kind": "topk", "name": "topk_k%d_%s" % (k, src.cfg["name"]),
+        self.cfg = {"kind": "topk",
+                    "name": "topk_%sk%d_%s" % ("ws_" if self.split else "", k, src.cfg["name"]),
                     "rows": rows, "cols": cols, "k": k}
         self.host = src.host
         self.bytes = rows * cols * 4 + rows * k * 4
@@ -189,11 +194,19 @@ class TopkWorkload:
         self.sets = [logits] + [logits.clone() for _ in range(nsets - 1)]
         self.outs = [torch.empty((rows, k), dtype=torch.int32, device="cuda") for _ in range(nsets)]
         self.nsets = nsets
+        self.ws = None
+        if self.split:
+            from sparse_attention_indexer_scaled_amd import topk_workspace_size
+            self.ws = torch.empty(topk_workspace_size(rows, cols), dtype=torch.uint8, device="cuda")
         del src
 
     def call(self, i):
-        from sparse_attention_indexer_scaled_amd import topk_indices
-        topk_indices(self.sets[i % self.nsets], self.k, indices=self.outs[i % self.nsets])
+        from sparse_attention_indexer_scaled_amd import topk_indices, topk_indices_ws
+        if self.split:
+            topk_indices_ws(self.sets[i % self.nsets], self.k, indices=self.outs[i % self.nsets],
+                            workspace=self.ws)
+        else:
+            topk_indices(self.sets[i % self.nsets], self.k, indices=self.outs[i % self.nsets])
 
 
 class KcacheWorkload:
@@ -267,7 +280,7 @@ class FusedTopkWorkload:
 
 
 def make_workload(idx, hot, tunables=None):
-    if idx in TOPK_WORKLOADS:
+    if idx in TOPK_WORKLOADS or idx in TOPK_WS_WORKLOADS:
         return TopkWorkload(idx, hot)
     if idx in FUSED_WORKLOADS:
         return FusedTopkWorkload(idx, hot, tunables)
@@ -749,8 +762,8 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 22, 4, 3, 0, 5, 6, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20,
-                     21) if i != args.workload]
+        [i for i in (1, 22, 4, 3, 0, 5, 6, 23, 24, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18,
+                     19, 20, 21) if i != args.workload]
     results, head, cpu = {}, None, {}
     for idx in order:
         wl = make_workload(idx, args.hot, tun)

@@ -203,6 +203,36 @@ int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *in
                      hipStream_t stream);
 
 /*
+ * mqa_topk_indices with a caller workspace: the same output for every input.
+ * mqa_topk_indices gives each row to one workgroup, and one CU streams a row
+ * at the rate its outstanding misses allow, so a few long rows leave most of
+ * the GPU idle.  With the workspace, long rows (more than 8192 columns, 16-byte
+ * aligned: cols a multiple of 4 and logits 16-byte aligned) are split over
+ * several workgroups each when there are too few rows to fill the GPU: each
+ * keeps the entries of its slice at or above the row's sampled threshold in
+ * the row's workspace region, then one workgroup per row gathers and sorts
+ * them; a row the sample misjudges is selected from its logits in full.  Other
+ * shapes run the one-workgroup-per-row path.
+ *
+ *   workspace  DEVICE memory of at least mqa_topk_workspace_size(rows, cols)
+ *              bytes (8 bytes per row and column plus 256 bytes per row),
+ *              256-byte aligned, owned by the caller; contents on entry do not
+ *              matter and are clobbered.  Calls that overlap on one workspace
+ *              race.  NULL (any workspace_bytes) runs the one-workgroup-per-row
+ *              path.
+ *
+ * Errors as for mqa_topk_indices, plus: a non-NULL workspace that is not
+ * 256-byte aligned or is smaller than asked for -> MQA_ERR_INVALID_ARG.
+ */
+int mqa_topk_indices_ws(const float *logits, int rows, int cols, int k, int32_t *indices,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes mqa_topk_indices_ws needs for rows x cols (0 when rows or
+ * cols is not positive, or the size would exceed 2^60).  Host-only, never
+ * fails. */
+size_t mqa_topk_workspace_size(int rows, int cols);
+
+/*
  * Fused paged decode + row-wise top-k: the indices mqa_topk_indices would
  * return for the logits paged_mqa_logits_decode (clean_logits = 1) would
  * write, without writing those logits (the top-k is the indexer's consumer:

@@ -25,4 +25,6 @@ from ._native import (  # noqa: F401
     paged_mqa_topk_decode_noalloc,
     paged_mqa_topk_workspace_size,
     topk_indices,
+    topk_indices_ws,
+    topk_workspace_size,
 )

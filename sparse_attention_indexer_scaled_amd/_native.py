@@ -24,7 +24,8 @@ MQA_ERR_LAUNCH = -3
 MQA_ERR_DEVICE = -4
 
 EXPORTED = ("mqa_is_supported", "mqa_logits_prefill", "paged_mqa_logits_decode",
-            "mqa_topk_indices", "paged_mqa_topk_decode", "paged_mqa_topk_decode_noalloc",
+            "mqa_topk_indices", "mqa_topk_indices_ws", "mqa_topk_workspace_size",
+            "paged_mqa_topk_decode", "paged_mqa_topk_decode_noalloc",
             "paged_mqa_topk_workspace_size", "mqa_kcache_quantize_insert", "mqa_last_error")
 # bytes of the library's static scratch (MQA_NOALLOC_SCRATCH_BYTES in the header)
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -71,6 +72,10 @@ def load_library(path: str = LIB_PATH):
     lib.paged_mqa_logits_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, P]
     lib.mqa_topk_indices.restype = I
     lib.mqa_topk_indices.argtypes = [P, I, I, I, P, P]
+    lib.mqa_topk_indices_ws.restype = I
+    lib.mqa_topk_indices_ws.argtypes = [P, I, I, I, P, P, ctypes.c_size_t, P]
+    lib.mqa_topk_workspace_size.restype = ctypes.c_size_t
+    lib.mqa_topk_workspace_size.argtypes = [I, I]
     lib.paged_mqa_topk_decode.restype = I
     lib.paged_mqa_topk_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P,
                                           ctypes.c_size_t, P, P]
@@ -207,6 +212,35 @@ def topk_indices(logits: torch.Tensor, k: int, indices: Optional[torch.Tensor] =
     rc = load_library().mqa_topk_indices(
         _dev(logits, "logits", torch.float32), rows, cols, int(k),
         _dev(indices, "indices", torch.int32), _stream(stream, logits.device))
+    _check(rc)
+    return indices
+
+
+def topk_workspace_size(rows: int, cols: int) -> int:
+    return int(load_library().mqa_topk_workspace_size(int(rows), int(cols)))
+
+
+def topk_indices_ws(logits: torch.Tensor, k: int, indices: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """topk_indices with a workspace (mqa_topk_indices_ws): the same indices;
+    long rows are split over several workgroups.  workspace: a uint8 device
+    tensor of at least topk_workspace_size(rows, cols) bytes (allocated from
+    torch's caching allocator when not given)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, cols]")
+    rows, cols = logits.shape
+    if indices is None:
+        indices = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    if indices.shape != (rows, k):
+        raise ValueError("indices must be [rows, k]")
+    if workspace is None:
+        workspace = torch.empty(max(topk_workspace_size(rows, cols), 1), dtype=torch.uint8,
+                                device=logits.device)
+    ws = _bytes(workspace, "workspace")
+    rc = load_library().mqa_topk_indices_ws(
+        _dev(logits, "logits", torch.float32), rows, cols, int(k),
+        _dev(indices, "indices", torch.int32), _dev(ws, "workspace"), ws.numel(),
+        _stream(stream, logits.device))
     _check(rc)
     return indices
 

@@ -388,6 +388,9 @@ extern "C" int paged_mqa_topk_decode(const uint8_t *q_fp8, const uint8_t *kv_cac
         return fail(MQA_ERR_INVALID_ARG, "the fused top-k runs the default ring depth (0 or %d "
                     "for this shape)", depth);
     if (batch > 0 && max_model_len > 0 && next_n >= 1 && next_n <= 8) {
+        if ((int64_t)batch * next_n > INT32_MAX)
+            return fail(MQA_ERR_INVALID_ARG, "batch %d x next_n %d rows exceed INT32_MAX", batch,
+                        next_n);
         if (!indices || !workspace)
             return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
         if (!aligned(indices, 4) || !aligned(workspace, 256))
@@ -512,6 +515,77 @@ extern "C" int paged_mqa_topk_decode_noalloc(const uint8_t *q_fp8, const uint8_t
                                  batch, next_n, num_heads, head_dim, kv_block_size, kv_layout,
                                  num_blocks, max_blocks_per_seq, max_model_len, k, ws,
                                  kNoAllocScratchBytes, tun, stream);
+}
+
+namespace {
+
+// The split top-k's workgroups per row: about six 4-wave workgroups per CU
+// over all rows, each slice at least 4096 columns; 1 = the one-row path.
+// 96 rows of 131072 columns (16 per row): 31.3 us against 32.4 at 8 per row
+// and 36-37 at 32, one GPU.
+constexpr int kTopkSplitTarget = 1536;
+constexpr int kTopkMinSlice4 = 1024;  // 16-byte groups
+
+int topk_split_of(int rows, int cols, const float *logits)
+{
+    if (cols <= 8192 || (cols & 3) != 0 || !aligned(logits, 16) || rows >= kTopkSplitTarget / 2)
+        return 1;
+    const int64_t want = ceil_div(kTopkSplitTarget, rows);
+    const int64_t cap = std::min<int64_t>(mqa::kTopkMaxSplit, (cols / 4) / kTopkMinSlice4);
+    return (int)std::max<int64_t>(1, std::min(want, cap));
+}
+
+} // namespace
+
+extern "C" size_t mqa_topk_workspace_size(int rows, int cols)
+{
+    if (rows <= 0 || cols <= 0 || (double)rows * ((double)cols + 64) * 8 > 1152921504606846976.0)
+        return 0;
+    return mqa::topk_split_workspace(nullptr, rows, cols).bytes;
+}
+
+extern "C" int mqa_topk_indices_ws(const float *logits, int rows, int cols, int k,
+                                   int32_t *indices, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    if (!workspace)
+        return mqa_topk_indices(logits, rows, cols, k, indices, stream);
+    if (rows < 0 || cols < 0)
+        return fail(MQA_ERR_INVALID_ARG, "rows=%d, cols=%d must be >= 0", rows, cols);
+    if (k < 1 || k > mqa::kMaxTopK)
+        return fail(MQA_ERR_INVALID_ARG, "k must be in 1..%d (got %d)", mqa::kMaxTopK, k);
+    if (rows == 0)
+        return ok();
+    if (!aligned(workspace, 256))
+        return fail(MQA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t need = mqa_topk_workspace_size(rows, cols);
+    if (cols > 0 && (need == 0 || workspace_bytes < need))
+        return fail(MQA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes "
+                    "mqa_topk_workspace_size asks for", workspace_bytes, need);
+    const int split = topk_split_of(rows, cols, logits);
+    if (split < 2)
+        return mqa_topk_indices(logits, rows, cols, k, indices, stream);
+    if (!indices || !logits)
+        return fail(MQA_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(indices, 4))
+        return fail(MQA_ERR_INVALID_ARG, "logits and indices must be 4-byte aligned");
+    if (int rc = check_device())
+        return rc;
+    mqa::TopkSplitLaunch p;
+    p.logits = logits;
+    p.indices = indices;
+    p.rows = rows;
+    p.cols = cols;
+    p.k = k;
+    p.split = split;
+    p.slice4 = (int)ceil_div(cols / 4, split);
+    p.ws = mqa::topk_split_workspace(workspace, rows, cols);
+    if (trace_on())
+        std::fprintf(stderr, "[mqa] topk rows=%d cols=%d k=%d split=%d\n", rows, cols, k, split);
+    hipError_t e = mqa::launch_topk_split(p, stream);
+    if (e != hipSuccess)
+        return fail(MQA_ERR_LAUNCH, "topk launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 extern "C" int mqa_topk_indices(const float *logits, int rows, int cols, int k, int32_t *indices,

@@ -107,6 +107,41 @@ struct TopkLaunch {
     int k;  // 1..kMaxTopK
 };
 
+// Split row top-k (mqa_topk_indices_ws): the workspace holds each row's
+// segments (an entry region of ent_stride >= cols entries per row) and the
+// slices' counts.
+constexpr int kTopkMaxSplit = 64;
+
+struct TopkSplitWorkspace {
+    uint64_t *entries;  // [rows][ent_stride]
+    int *counts;        // [rows][split]
+    int64_t ent_stride;
+    size_t bytes;
+};
+
+inline TopkSplitWorkspace topk_split_workspace(void *base, int rows, int cols)
+{
+    TopkSplitWorkspace w;
+    w.ent_stride = ((int64_t)cols + 63) / 64 * 64;
+    const size_t ent = fused_align((size_t)rows * w.ent_stride * 8);
+    char *b = static_cast<char *>(base);
+    w.entries = reinterpret_cast<uint64_t *>(b);
+    w.counts = reinterpret_cast<int *>(b ? b + ent : nullptr);
+    w.bytes = ent + fused_align((size_t)rows * kTopkMaxSplit * 4);
+    return w;
+}
+
+struct TopkSplitLaunch {
+    const float *logits;  // [rows, cols], 16-byte aligned rows (cols % 4 == 0)
+    int32_t *indices;
+    int rows;
+    int cols;
+    int k;
+    int split;   // workgroups per row, 2..kTopkMaxSplit
+    int slice4;  // 16-byte groups per workgroup
+    TopkSplitWorkspace ws;
+};
+
 // Fused top-k steps after the sampling decode and before the filtering one
 // (thresholds from the sample), and after it (select, or flag the row).
 struct FusedTopkLaunch {
@@ -150,6 +185,7 @@ hipError_t launch_decode_d64(const DecodeLaunch &p, hipStream_t stream);    // h
 hipError_t launch_decode_fused(const DecodeLaunch &p, hipStream_t stream);  // modes 1 and 2
 hipError_t launch_decode_fused_d64(const DecodeLaunch &p, hipStream_t stream);  // at head dim 64
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream);
+hipError_t launch_topk_split(const TopkSplitLaunch &p, hipStream_t stream);
 hipError_t launch_fused_threshold(const FusedTopkLaunch &p, hipStream_t stream);
 hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream);
 hipError_t launch_kcache_insert(const KcacheLaunch &p, hipStream_t stream);

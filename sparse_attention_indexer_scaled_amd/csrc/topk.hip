@@ -882,6 +882,191 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     sort_and_write(sh, n, out, k, tid, lane, wave);
 }
 
+// ---- split row top-k (mqa_topk_indices_ws) ---------------------------------
+// One workgroup per row streams the row at one CU's read rate, which its
+// outstanding misses cap near 30-40 GB/s, so with fewer rows than CUs most of
+// the GPU idles.  With a caller workspace the row is split: `split`
+// workgroups of kSplitThreads threads per row each take the row's threshold
+// from the same sample (so all of them find the same key), keep the entries of
+// their slice at or above it in their own segment of the row's workspace region
+// and count them; then one workgroup per row gathers the segments and sorts
+// them as the one-row path does.  A row whose segments cannot hold its top k
+// (the sample misjudged it, or it has too few listable entries) is selected
+// from its logits in full by that workgroup, so the output is the one-row
+// path's for every input.
+constexpr int kSplitThreads = 256;
+// 16-byte groups per thread and batch (16 KiB per workgroup; the first batch is
+// requested before the sampling).  Measured on 96 rows of 131072 columns, one
+// GPU: 31.3 us at 4 with 16 workgroups per row, 31.9 at 8 with 8, 35.2 with the
+// whole slice in one batch of 16 (its loads then delay the sample's); 32 or 64
+// workgroups per row repeat the sampling too often (36-49 us).
+constexpr int kSplitUnroll = 4;
+
+struct SplitShared {
+    uint32_t hist[kMaxBins];
+    int bcast[4];
+    int wave_total[kSplitThreads / 64];
+    int count;
+};
+
+// Workgroup (row r, slice c): groups [c slice4, (c + 1) slice4) of the row's
+// cols / 4 16-byte groups (the row is 16-byte aligned and cols a multiple of
+// 4).  Its segment starts at entry 4 c slice4 of the row's region, so it holds
+// the slice's survivors whatever their number.  counts[r][c] is the number
+// kept, or -1 when the sample gives no threshold.
+__global__ __launch_bounds__(kSplitThreads) void topk_split_filter_kernel(
+    const float *__restrict__ logits, int cols, int k, int split, int slice4,
+    uint64_t *__restrict__ entries, int64_t ent_stride, int *__restrict__ counts)
+{
+    __shared__ SplitShared sh;
+    constexpr int U = kSplitUnroll;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x / split, c = blockIdx.x % split;
+    const float *x = logits + (int64_t)r * cols;
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    const int n4 = cols >> 2;
+    const int g0 = min(c * slice4, n4), g1 = min(g0 + slice4, n4);
+    const int nb = (g1 - g0 + U * kSplitThreads - 1) / (U * kSplitThreads);
+    RowSample<kSplitThreads> rs;
+    sample_load<kSplitThreads, true>(rs, x, cols, tid);
+    // the slice's first batch, requested behind the sample (groups past the
+    // slice read its last group and are dropped by index)
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = x4[max(min(g0 + u * kSplitThreads + tid, g1 - 1), 0)];
+    if (tid == 0)
+        sh.count = 0;
+    const uint32_t t0 = sample_threshold(sh, rs, cols, k, tid, lane, wave);
+    int *cnt = counts + (int64_t)r * split + c;
+    if (t0 == 0u) {  // uniform
+        if (tid == 0)
+            *cnt = -1;
+        return;
+    }
+    const float f0 = key_value(max(t0, 0x00800000u));
+    uint64_t *seg = entries + (int64_t)r * ent_stride + 4 * (int64_t)g0;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    // keep the batch's entries >= f0: one LDS atomic per wave for the slots
+    auto emit = [&](int j) {
+        int i[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            i[u] = g0 + j * U * kSplitThreads + u * kSplitThreads + tid;
+            ok[u] = i[u] < g1;
+        }
+        int total = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            total += __popcll(__ballot(ok[u] && v[u].x >= f0)) +
+                     __popcll(__ballot(ok[u] && v[u].y >= f0)) +
+                     __popcll(__ballot(ok[u] && v[u].z >= f0)) +
+                     __popcll(__ballot(ok[u] && v[u].w >= f0));
+        if (total == 0)
+            return;
+        int base = 0;
+        if (lane == 0)
+            base = atomicAdd(&sh.count, total);
+        base = __builtin_amdgcn_readfirstlane(base);
+        auto put = [&](bool keep, float f, int col) {
+            const uint64_t b = __ballot(keep);
+            if (keep)
+                seg[base + __popcll(b & lt)] = entry(order_key(f), col);
+            base += __popcll(b);
+        };
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            put(ok[u] && v[u].x >= f0, v[u].x, 4 * i[u]);
+            put(ok[u] && v[u].y >= f0, v[u].y, 4 * i[u] + 1);
+            put(ok[u] && v[u].z >= f0, v[u].z, 4 * i[u] + 2);
+            put(ok[u] && v[u].w >= f0, v[u].w, 4 * i[u] + 3);
+        }
+    };
+    emit(0);
+    for (int j = 1; j < nb; ++j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = x4[min(g0 + j * U * kSplitThreads + u * kSplitThreads + tid, g1 - 1)];
+        emit(j);
+    }
+    __syncthreads();
+    if (tid == 0)
+        *cnt = sh.count;
+}
+
+// Row r: gather its segments (their prefix over the slices) and sort, or, when
+// some slice had no threshold or the segments cannot hold the top k, select
+// from the logits row in full.
+__global__ __launch_bounds__(kThreads) void topk_split_select_kernel(
+    const float *__restrict__ logits, int cols, int k, int split, int slice4,
+    const uint64_t *__restrict__ entries, int64_t ent_stride, const int *__restrict__ counts,
+    int32_t *__restrict__ indices)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
+    TopkShared &sh = *reinterpret_cast<TopkShared *>(topk_lds);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x;
+    const float *x = logits + (int64_t)r * cols;
+    const uint64_t *row = entries + (int64_t)r * ent_stride;
+    int32_t *out = indices + (int64_t)r * k;
+    const int c = tid < split ? counts[(int64_t)r * split + tid] : 0;
+    const bool none = __syncthreads_or(c < 0);
+    const int cc = max(c, 0);
+    const int incl = wave_inclusive_scan(cc, lane);
+    if (lane == 63)
+        sh.wave_total[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        before += w < wave ? sh.wave_total[w] : 0;
+        total += sh.wave_total[w];
+    }
+    if (tid < split)
+        sh.hist[tid] = (uint32_t)(before + incl - cc);
+    __syncthreads();
+    int n;
+    if (!none && total >= k && total <= kSortCap) {  // uniform
+        // entry i (in slice order) belongs to the last slice whose prefix is
+        // <= i; every thread finds the sources of its entries first, then
+        // issues all their loads
+        constexpr int EPT = kSortCap / kThreads;
+        int64_t src[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = tid + e * kThreads;
+            src[e] = -1;
+            if (i < total) {
+                int lo = 0, hi = split - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if ((int)sh.hist[mid] <= i)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                src[e] = 4 * (int64_t)slice4 * lo + (i - (int)sh.hist[lo]);
+            }
+        }
+        uint64_t v[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            v[e] = src[e] >= 0 ? row[src[e]] : 0ull;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (src[e] >= 0)
+                sh.buf[tid + e * kThreads] = v[e];
+        n = total;
+    } else {
+        if (tid == 0)
+            sh.count = 0;
+        __syncthreads();
+        n = radix_select(sh, x, cols, k, tid, lane, wave);
+    }
+    __syncthreads();
+    sort_and_write(sh, n, out, k, tid, lane, wave);
+}
+
 // ---- fused decode top-k -------------------------------------------------
 // The decode kernel's sample mode leaves kFusedSampleCols logits per row (-inf
 // outside the window); its filter mode then keeps, per row, every entry at or
@@ -1196,6 +1381,25 @@ hipError_t launch_fused_select(const FusedTopkLaunch &p, hipStream_t stream)
     case 4064: return launch_fused_select_ht<4, 64>(p, ra, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_topk_split(const TopkSplitLaunch &p, hipStream_t stream)
+{
+    static std::atomic<uint64_t> raised{0};
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&topk_split_select_kernel),
+                                   (int)sizeof(TopkShared), raised);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(topk_split_filter_kernel, dim3(p.rows * p.split), dim3(kSplitThreads), 0,
+                       stream, p.logits, p.cols, p.k, p.split, p.slice4, p.ws.entries,
+                       p.ws.ent_stride, p.ws.counts);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(topk_split_select_kernel, dim3(p.rows), dim3(kThreads), sizeof(TopkShared),
+                       stream, p.logits, p.cols, p.k, p.split, p.slice4, p.ws.entries,
+                       p.ws.ent_stride, p.ws.counts, p.indices);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkLaunch &p, hipStream_t stream)

@@ -190,6 +190,22 @@ def test_fused_topk_workspace_size(lib):
     assert mqa.paged_mqa_topk_workspace_size(16, 6, 131072) == big
 
 
+def test_topk_workspace_size_and_validation(lib):
+    ws = lib.mqa_topk_workspace_size
+    assert ws(0, 10) == 0 and ws(10, 0) == 0 and ws(-1, 10) == 0
+    big = ws(96, 131072)
+    assert 96 * 131072 * 8 <= big <= 96 * 131072 * 8 + 96 * 64 * 4 + 2 * 256
+    assert mqa.topk_workspace_size(96, 131072) == big
+    E = mqa._native
+    f = lib.mqa_topk_indices_ws
+    assert f(None, 4, 100, 0, None, None, 0, None) == E.MQA_ERR_INVALID_ARG  # k, NULL workspace
+    assert f(None, 0, 100, 5, None, ctypes.c_void_p(256), 0, None) == E.MQA_OK  # no rows
+    assert f(None, 4, 100, 5, None, ctypes.c_void_p(1000), 1 << 20, None) == E.MQA_ERR_INVALID_ARG
+    assert "256-byte" in mqa.last_error()
+    assert f(None, 4, 100, 5, None, ctypes.c_void_p(4096), 16, None) == E.MQA_ERR_INVALID_ARG
+    assert "smaller than" in mqa.last_error()
+
+
 def _fused(lib, ptrs, B=2, nn=1, H=32, D=128, bs=64, nb=4, mbps=2, mml=128, k=16, ws=None,
            wsb=0, tun=None, layout=0):
     return lib.paged_mqa_topk_decode(*ptrs, B, nn, H, D, bs, layout, nb, mbps, mml, k, ws, wsb,
@@ -227,6 +243,9 @@ def test_fused_topk_validation(lib):
     assert _fused(lib, nulls, mml=0) == 0
     assert _fused(lib, nulls) == E.MQA_ERR_INVALID_ARG
     assert "NULL" in mqa.last_error()
+    # batch x next_n past INT32_MAX: a clear error, not a wrapped row count
+    assert _fused(lib, nulls, B=2**30, nn=2) == E.MQA_ERR_INVALID_ARG
+    assert "INT32_MAX" in mqa.last_error()
     need = lib.paged_mqa_topk_workspace_size(2, 1, 128)
     fake = [P(0x10000)] * 6  # never dereferenced: rejected before the device is touched
     assert _fused(lib, fake, ws=P(0x20080), wsb=need) == E.MQA_ERR_INVALID_ARG

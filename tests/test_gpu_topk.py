@@ -1,4 +1,5 @@
-"""GPU parity of the row-wise top-k (mqa_topk_indices) with the oracle.
+"""GPU parity of the row-wise top-k (mqa_topk_indices, and mqa_topk_indices_ws,
+which splits long rows over several workgroups) with the oracle.
 
 Both sides select on the same fp32 logits, so every comparison is taken in
 fp32 on both and the outputs (column indices) must match bit for bit.
@@ -37,15 +38,28 @@ def gpu_topk(x, k):
     return out.cpu().numpy()
 
 
+def gpu_topk_ws(x, k):
+    """mqa_topk_indices_ws: long aligned rows split over several workgroups."""
+    t = dev(x)
+    out = torch.full((x.shape[0], k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.full((max(_native.topk_workspace_size(*x.shape), 1),), 0x7f, dtype=torch.uint8,
+                    device="cuda")  # stale contents must not matter
+    _native.topk_indices_ws(t, k, indices=out, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
 def check(x, k, tag):
-    got = gpu_topk(x, k)
+    """Both entry points against the oracle, bit for bit."""
     want = oracle_topk(x, k)
-    if not np.array_equal(got, want):
-        bad = np.nonzero((got != want).any(axis=1))[0]
-        r = int(bad[0])
-        j = int(np.nonzero(got[r] != want[r])[0][0])
-        raise AssertionError("%s: %d rows differ; row %d first at %d: gpu %s oracle %s" % (
-            tag, bad.size, r, j, got[r, j:j + 4], want[r, j:j + 4]))
+    for name, fn in (("one-row", gpu_topk), ("workspace", gpu_topk_ws)):
+        got = fn(x, k)
+        if not np.array_equal(got, want):
+            bad = np.nonzero((got != want).any(axis=1))[0]
+            r = int(bad[0])
+            j = int(np.nonzero(got[r] != want[r])[0][0])
+            raise AssertionError("%s (%s): %d rows differ; row %d first at %d: gpu %s oracle %s"
+                                 % (tag, name, bad.size, r, j, got[r, j:j + 4], want[r, j:j + 4]))
 
 
 @pytest.mark.parametrize("cols", [1, 7, 100, 4096, 33000, 131072])
@@ -123,6 +137,20 @@ def test_zero_columns_writes_minus_one():
 
 def test_zero_rows_is_a_no_op():
     _native.topk_indices(torch.empty((0, 10), dtype=torch.float32, device="cuda"), 4)
+    _native.topk_indices_ws(torch.empty((0, 10), dtype=torch.float32, device="cuda"), 4)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 8196), (2, 131072), (7, 100000), (767, 16384)])
+def test_split_row_counts_and_widths(rows, cols):
+    """The split path at its edges: the shortest split row, a few rows of the
+    benchmark's width, slices that do not divide the row, and the largest row
+    count that still splits (767 rows of 16384 columns, two workgroups each)."""
+    rng = np.random.default_rng(560 + rows)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[:, rng.integers(0, cols, 50)] = 9.0  # ties across slices
+    say("topk split rows=%d cols=%d" % (rows, cols))
+    for k in (1, 512, 2048):
+        check(x, k, "split rows=%d cols=%d k=%d" % (rows, cols, k))
 
 
 def _bucketed_row(cols, rng):

@@ -2,9 +2,11 @@
 batch 16, next_n 6, context 131072, k = 2048 and 512 (the two index_topk values
 of the pages).
 
-- The one-row top-k (mqa_topk_indices) ranks the oracle's logits of that
-  workload (fp64, rounded once to fp32) and must equal the oracle's top-k of
-  the same fp32 array bit for bit: both sides take every comparison in fp32.
+- The one-row top-k (mqa_topk_indices) and the workspace call that splits
+  each row over several workgroups (mqa_topk_indices_ws) rank the oracle's
+  logits of that workload (fp64, rounded once to fp32) and must equal the
+  oracle's top-k of the same fp32 array bit for bit: both sides take every
+  comparison in fp32.
 - The fused decode top-k and the unfused pipeline (decode call, then the
   one-row top-k) rank the GPU's own logits, which differ from the oracle's
   within the fp32 parity bound tau = 1e-5 * M per element (M the oracle on
@@ -58,11 +60,21 @@ def test_one_row_topk_of_the_oracle_logits(headline, k):
     _, ref, _ = headline
     x = ref.astype(np.float32)
     say("topk of the headline's oracle logits k=%d" % k)
+    want = oracle_topk(x, k)
+    t = dev(x)
     out = torch.full((x.shape[0], k), -7, dtype=torch.int32, device="cuda")
-    _native.topk_indices(dev(x), k, indices=out)
+    _native.topk_indices(t, k, indices=out)
     torch.cuda.synchronize()
-    got, want = out.cpu().numpy(), oracle_topk(x, k)
+    got = out.cpu().numpy()
     assert np.array_equal(got, want), _first_diff(got, want, "k=%d" % k)
+    # the workspace call splits each of these rows over several workgroups
+    out.fill_(-7)
+    ws = torch.full((_native.topk_workspace_size(*x.shape),), 0x5a, dtype=torch.uint8,
+                    device="cuda")
+    _native.topk_indices_ws(t, k, indices=out, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got, want), _first_diff(got, want, "workspace call k=%d" % k)
 
 
 def _assert_valid_topk(idx, ref, tau, k, tag):
