@@ -825,6 +825,90 @@ __device__ int radix_select(TopkShared &sh, const float *x, int cols, int k, int
     return k;
 }
 
+// ---- segment gather (the selects of the fused and the split top-k) --------
+// A row's survivors sit in `split` segments of its entry region, segment s
+// starting at entry seg_start(s) with counts[s] entries, and the select wants
+// them in segment order in sh.buf.  Thread t requests entries
+// j = t % L + L e (e < kWinLoads, L = kThreads / split) of segment t / L as the
+// workgroup starts, beside the counts: a window of W = L kWinLoads entries at
+// the head of every segment, read before its count is known (what lies past
+// the count is ignored; every read stays inside the row's region).  Once the
+// counts' prefix is in sh.hist the windows' entries go straight to their
+// places, and only segments longer than W take a second round of loads.
+constexpr int kWinLoads = 8;
+
+struct SegWindow {
+    uint64_t v[kWinLoads];
+    int seg, j0, L;
+};
+
+template <class SegStart>
+__device__ __forceinline__ void window_request(SegWindow &g, const uint64_t *row, int64_t limit,
+                                               int split, SegStart seg_start, int tid)
+{
+    g.L = max(kThreads / split, 1);
+    g.seg = tid / g.L;
+    g.j0 = tid - g.seg * g.L;
+    const int64_t base = seg_start(min(g.seg, split - 1)) + g.j0;
+#pragma unroll
+    for (int e = 0; e < kWinLoads; ++e)
+        g.v[e] = row[min(base + (int64_t)g.L * e, limit - 1)];
+}
+
+// Puts the n entries in segment order into sh.buf: window entries (W = the
+// window length, 0 when the windows were read at other starts than
+// seg_start's) from registers, the rest of every segment longer than W
+// (`over`: some segment is, the same in every thread) by a binary search over
+// the prefix in sh.hist and one round of loads.
+template <class SegStart>
+__device__ __forceinline__ void window_place(TopkShared &sh, const SegWindow &g, const uint64_t *row,
+                                             int split, int n, SegStart seg_start, int W, bool over,
+                                             int tid)
+{
+    if (W > 0 && g.seg < split) {
+        const int st = (int)sh.hist[g.seg];
+        const int cnt = (g.seg + 1 < split ? (int)sh.hist[g.seg + 1] : n) - st;
+#pragma unroll
+        for (int e = 0; e < kWinLoads; ++e) {
+            const int j = g.j0 + g.L * e;
+            if (j < cnt)
+                sh.buf[st + j] = g.v[e];
+        }
+    }
+    if (!over)
+        return;
+    // entry i (in segment order) belongs to the last segment whose prefix is
+    // <= i (empty segments share their successor's prefix)
+    constexpr int EPT = kSortCap / kThreads;
+    int64_t src[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = tid + e * kThreads;
+        src[e] = -1;
+        if (i < n) {
+            int lo = 0, hi = split - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int)sh.hist[mid] <= i)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int j = i - (int)sh.hist[lo];
+            if (j >= W)
+                src[e] = seg_start(lo) + j;
+        }
+    }
+    uint64_t v[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        v[e] = src[e] >= 0 ? row[src[e]] : 0ull;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        if (src[e] >= 0)
+            sh.buf[tid + e * kThreads] = v[e];
+}
+
 // Sort the n entries gathered in sh.buf (n <= kSortCap; they hold the row's
 // top min(n, k)) and write the row's k output columns.
 __device__ __forceinline__ void sort_and_write(TopkShared &sh, int n, int32_t *out, int k, int tid,
@@ -1010,7 +1094,11 @@ __global__ __launch_bounds__(kThreads) void topk_split_select_kernel(
     const float *x = logits + (int64_t)r * cols;
     const uint64_t *row = entries + (int64_t)r * ent_stride;
     int32_t *out = indices + (int64_t)r * k;
-    const int c = tid < split ? counts[(int64_t)r * split + tid] : 0;
+    const int c_in = counts[(int64_t)r * split + min(tid, split - 1)];
+    const auto seg_start = [&](int g) { return 4 * (int64_t)slice4 * g; };
+    SegWindow win;
+    window_request(win, row, ent_stride, split, seg_start, tid);
+    const int c = tid < split ? c_in : 0;
     const bool none = __syncthreads_or(c < 0);
     const int cc = max(c, 0);
     const int incl = wave_inclusive_scan(cc, lane);
@@ -1024,38 +1112,11 @@ __global__ __launch_bounds__(kThreads) void topk_split_select_kernel(
     }
     if (tid < split)
         sh.hist[tid] = (uint32_t)(before + incl - cc);
-    __syncthreads();
+    const int W = win.L * kWinLoads;
+    const bool over = __syncthreads_or(cc > W);
     int n;
     if (!none && total >= k && total <= kSortCap) {  // uniform
-        // entry i (in slice order) belongs to the last slice whose prefix is
-        // <= i; every thread finds the sources of its entries first, then
-        // issues all their loads
-        constexpr int EPT = kSortCap / kThreads;
-        int64_t src[EPT];
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int i = tid + e * kThreads;
-            src[e] = -1;
-            if (i < total) {
-                int lo = 0, hi = split - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if ((int)sh.hist[mid] <= i)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
-                }
-                src[e] = 4 * (int64_t)slice4 * lo + (i - (int)sh.hist[lo]);
-            }
-        }
-        uint64_t v[EPT];
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            v[e] = src[e] >= 0 ? row[src[e]] : 0ull;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            if (src[e] >= 0)
-                sh.buf[tid + e * kThreads] = v[e];
+        window_place(sh, win, row, split, total, seg_start, W, over, tid);
         n = total;
     } else {
         if (tid == 0)
@@ -1119,6 +1180,14 @@ __global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
     __shared__ ThresholdShared sh;
     const int tid = threadIdx.x;
     const int r = blockIdx.x;
+    // The sample (every row's is written) is requested together with the
+    // context length, so the two loads share one round of memory latency.
+    constexpr int EPT = kFusedSampleCols / kThresholdThreads;
+    const float *x = sample + (int64_t)r * kFusedSampleCols + EPT * tid;
+    float4 f[EPT / 4];
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j)
+        f[j] = *reinterpret_cast<const float4 *>(x + 4 * j);
     const int pop = row_population(ctx_lens, r, next_n, mml);
     if (pop <= kSortCap) {
         // short row: keep every listable entry (key >= 1)
@@ -1126,18 +1195,16 @@ __global__ __launch_bounds__(kThresholdThreads) void fused_threshold_kernel(
             threshold[r] = 1u;
         return;
     }
-    constexpr int EPT = kFusedSampleCols / kThresholdThreads;
-    const float *x = sample + (int64_t)r * kFusedSampleCols + EPT * tid;
     uint32_t samp[EPT];
     int mine = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; j += 4) {
-        const float4 f = *reinterpret_cast<const float4 *>(x + j);
-        samp[j + 0] = order_key(f.x);
-        samp[j + 1] = order_key(f.y);
-        samp[j + 2] = order_key(f.z);
-        samp[j + 3] = order_key(f.w);
-        mine += (samp[j] != 0u) + (samp[j + 1] != 0u) + (samp[j + 2] != 0u) + (samp[j + 3] != 0u);
+    for (int j = 0; j < EPT / 4; ++j) {
+        samp[4 * j + 0] = order_key(f[j].x);
+        samp[4 * j + 1] = order_key(f[j].y);
+        samp[4 * j + 2] = order_key(f[j].z);
+        samp[4 * j + 3] = order_key(f[j].w);
+        mine += (samp[4 * j] != 0u) + (samp[4 * j + 1] != 0u) + (samp[4 * j + 2] != 0u) +
+                (samp[4 * j + 3] != 0u);
     }
     if (tid == 0)
         sh.listable = 0;
@@ -1261,15 +1328,23 @@ __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
     const int wave = tid >> 6;
     const int r = blockIdx.x;
     const int b = r / ra.next_n;
-    const int pop = row_population(ra.ctx_lens, r, ra.next_n, ra.mml);
-    const int nvalid = max(min(ra.ctx_lens[b], ra.mml), 0);
-    const int nsteps = (nvalid + 63) / 64;
     const int *cnt = counts + (int64_t)r * split;
     uint64_t *row = ra.entries + (int64_t)r * ra.ent_stride;
     int32_t *out = indices + (int64_t)r * k;
+    // The counts and the segment windows are requested before the context
+    // length is known, the windows at the segment starts of a context that
+    // fills max_model_len; other rows gather every entry after the prefix.
+    const int c_in = cnt[min(tid, split - 1)];
+    const int64_t full_steps = ((int64_t)ra.mml + 63) / 64;
+    SegWindow win;
+    window_request(win, row, ra.ent_stride, split,
+                   [&](int s) { return full_steps * s / split * 64; }, tid);
+    const int pop = row_population(ra.ctx_lens, r, ra.next_n, ra.mml);
+    const int nvalid = max(min(ra.ctx_lens[b], ra.mml), 0);
+    const int nsteps = (nvalid + 63) / 64;
 
     // exclusive prefix of the segment counts (split <= kThreads) in sh.hist
-    const int c = tid < split ? cnt[tid] : 0;
+    const int c = tid < split ? c_in : 0;
     const int incl = wave_inclusive_scan(c, lane);
     if (lane == 63)
         sh.wave_total[wave] = incl;
@@ -1286,40 +1361,13 @@ __global__ __launch_bounds__(kThreads) void fused_select_kernel(FusedRowArgs ra,
     const bool ok = (total >= k || total == pop) && total <= kSortCap;
     if (tid == 0)
         recomputed[r] = ok ? 0 : 1;
-    __syncthreads();
+    // segment s starts at the first column of the filter workgroup s
+    const int W = nsteps == full_steps ? win.L * kWinLoads : 0;
+    const bool over = __syncthreads_or(c > W);
     int n;
     if (ok) {  // uniform
-        // Entry i (in segment order) belongs to the last segment whose prefix
-        // is <= i (empty segments share their successor's prefix); segment s
-        // starts at the first column of the filter workgroup s.  Every thread
-        // first finds the sources of its entries, then issues all their loads,
-        // so the gather costs one round of memory latency, not one per segment.
-        constexpr int EPT = kSortCap / kThreads;
-        int64_t src[EPT];
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int i = tid + e * kThreads;
-            src[e] = -1;
-            if (i < total) {
-                int lo = 0, hi = split - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if ((int)sh.hist[mid] <= i)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
-                }
-                src[e] = (int64_t)nsteps * lo / split * 64 + (i - (int)sh.hist[lo]);
-            }
-        }
-        uint64_t v[EPT];
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            v[e] = src[e] >= 0 ? row[src[e]] : 0ull;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            if (src[e] >= 0)
-                sh.buf[tid + e * kThreads] = v[e];
+        window_place(sh, win, row, split, total,
+                     [&](int s) { return (int64_t)nsteps * s / split * 64; }, W, over, tid);
         n = total;
     } else {
         // the row's own segment region (>= mml floats) now holds its logits

@@ -178,6 +178,34 @@ def test_fused_rows_the_sample_misjudges():
             assert np.array_equal(got[1], np.arange(2048))
 
 
+def _bunched_decode():
+    """Two long sequences (one full, one 5000 tokens short of max_model_len)
+    whose kv scales grow fourfold along the context, so that the largest
+    logits, and most entries the sampled threshold keeps, lie in the later
+    filter workgroups' segments."""
+    ctx = [131072, 126072]
+    d = inputs.make_decode(2, 2, ctx, 131072, seed=970, poison=True)
+    _, sview = inputs.cache_views(d.kv_cache, d.block_size, d.D)
+    for b, c in enumerate(ctx):
+        grow = (1.0 + 3.0 * np.arange(c) / c).astype(np.float32)
+        p = np.arange(c)
+        blocks = d.block_tables[b, p // d.block_size]
+        sview[blocks, p % d.block_size] *= grow
+        d.s_seq[b] = d.s_seq[b] * grow
+    return d
+
+
+def test_fused_survivors_bunched_in_few_segments():
+    """Segments holding far more kept entries than the select reads ahead of
+    the counts (the rest is gathered after them), and a shorter sequence
+    whose segments start elsewhere than a full context's."""
+    d = _bunched_decode()
+    dv = decode_device_inputs(d)
+    for k in (2048, 512):
+        say("fused topk bunched survivors k=%d" % k)
+        assert_same(fused(d, k, dv=dv), unfused(d, k, dv=dv), "bunched k=%d" % k)
+
+
 # Every other cache layout, head count and head dim the logits call takes:
 # (kv_block_size, num_heads, preshuffled, head_dim)
 LAYOUTS = [(16, 32, False, 128), (16, 32, True, 128), (128, 32, False, 128), (128, 32, True, 128),
