@@ -508,13 +508,13 @@ PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles
 
 
 KERNEL_SOURCES = {
-    "decode_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "decode_kernel.h",
-                      "decode.hip"),
-    "prefill_kernel": ("device.h", "launch.h", "api.cpp", "prefill.hip"),
+    "decode_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "ring.h",
+                      "decode_kernel.h", "decode.hip"),
+    "prefill_kernel": ("device.h", "launch.h", "api.cpp", "ring.h", "prefill.hip"),
     "topk_kernel": ("device.h", "launch.h", "order_key.h", "api.cpp", "topk.hip"),
     # the fused decode top-k: the decode template's sample and filter modes,
     # then the threshold and select kernels
-    "fused_topk": ("device.h", "launch.h", "order_key.h", "api.cpp", "decode_kernel.h",
+    "fused_topk": ("device.h", "launch.h", "order_key.h", "api.cpp", "ring.h", "decode_kernel.h",
                    "decode_fused.hip", "topk.hip"),
     "kcache_insert_kernel": ("device.h", "launch.h", "api.cpp", "kcache.hip"),
 }

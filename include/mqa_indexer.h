@@ -54,10 +54,20 @@ extern "C" {
  * the wave count are host-chosen and overridable.)
  *
  *   prefill:
- *     block_m      query rows that share one K stream per wave: 1, 2, 4 or 8
+ *     ring_depth   1 = every wave streams its own K into registers; 2..7 =
+ *                  a workgroup of 4 waves shares each K step through an LDS
+ *                  ring of that many steps (head_dim 128 only: 32 heads with
+ *                  4 rows per wave, 64 heads with 2 rows and depth 3 or 4;
+ *                  the default there, at depth 4, for all but small
+ *                  problems); 0 = the heuristic
+ *     block_m      query rows per wave: 1, 2, 4 or 8 (with the ring 4 at 32
+ *                  heads, 2 at 64)
  *     split_n      workgroups per row block along the columns, >= 1
- *     num_warps    waves per workgroup (they split the column range), 1..4
+ *     num_warps    waves per workgroup, 1..4: they split the column range
+ *                  (4 with the ring, where they split the rows instead)
  *     reverse_rows 1 = dispatch row blocks high-m first, -1 = natural order
+ *     (setting block_m or num_warps selects the per-wave kernel unless
+ *     ring_depth asks for the ring)
  *   decode:
  *     rows_per_block  next_n rows each wave computes, 1..4 (clamped to
  *                     next_n); a workgroup has ceil(next_n / rows_per_block)

@@ -24,6 +24,7 @@ struct PrefillLaunch {
     int reverse;   // 1: high-m row blocks first
     int head_tiles;  // num_heads / 32: 1, 2 or 4
     int head_dim;    // 64 or 128
+    int ring;        // 0: every wave streams its own K; else the shared-K ring's depth
 };
 
 struct DecodeLaunch {

@@ -249,9 +249,40 @@ def test_prefill_tunables_do_not_change_bits():
     base = run_prefill(p)
     for tun in [Tunables(block_m=1), Tunables(block_m=2, split_n=3), Tunables(block_m=8, num_warps=1),
                 Tunables(split_n=7, num_warps=2, reverse_rows=1), Tunables(reverse_rows=-1),
-                Tunables(block_m=4, split_n=40, num_warps=3)]:
+                Tunables(block_m=4, split_n=40, num_warps=3),
+                # the shared-K ring: 45 rows leave the last workgroup's last
+                # wave one row; 40 splits leave some parts without a step
+                Tunables(ring_depth=2), Tunables(ring_depth=4, split_n=3),
+                Tunables(ring_depth=7, split_n=1, reverse_rows=1), Tunables(ring_depth=5, split_n=40),
+                Tunables(ring_depth=1, split_n=2)]:
         say("prefill tunables %s" % [getattr(tun, f) for f, _ in Tunables._fields_])
         assert np.array_equal(run_prefill(p, tun=tun), base, equal_nan=True)
+
+
+@pytest.mark.parametrize("mode", ["causal", "cp", "misaligned", "empty", "past_end", "multi_req"])
+def test_prefill_ring_equals_per_wave_kernel(mode):
+    """The shared-K ring (the default at 32 heads, head dim 128) against the
+    per-wave kernel, bit for bit, with and without the -inf fill: a row count
+    that is no multiple of the 16-row workgroup and columns that end inside a
+    step."""
+    p = inputs.make_prefill(1000, 3000, seed=405, windows=mode)
+    for clean in (True, False):
+        want = run_prefill(p, clean=clean, tun=Tunables(ring_depth=1))
+        for tun in (None, Tunables(ring_depth=3, split_n=5)):
+            say("prefill ring mode=%s clean=%d" % (mode, clean))
+            assert np.array_equal(run_prefill(p, clean=clean, tun=tun), want, equal_nan=True)
+
+
+@pytest.mark.parametrize("mode", ["causal", "multi_req", "empty"])
+def test_prefill_ring_64_heads_equals_per_wave_kernel(mode):
+    """The 64-head shared-K ring (4 waves of 2 rows) against the per-wave
+    kernel, bit for bit."""
+    p = inputs.make_prefill(1000, 3000, seed=406, H=64, windows=mode)
+    for clean in (True, False):
+        want = run_prefill(p, clean=clean, tun=Tunables(ring_depth=1))
+        for tun in (None, Tunables(ring_depth=4), Tunables(ring_depth=3, split_n=5, reverse_rows=1)):
+            say("prefill ring 64 heads mode=%s clean=%d" % (mode, clean))
+            assert np.array_equal(run_prefill(p, clean=clean, tun=tun), want, equal_nan=True)
 
 
 def test_decode_tunables_do_not_change_bits():
