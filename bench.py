@@ -543,6 +543,12 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
+# Part of the dispatch name that picks a kernel's dispatches out of a
+# rocprofv3 run (both prefill kernels, the per-wave and the shared-K one,
+# start with "prefill_").
+KERNEL_NAME_PART = {"prefill_kernel": "prefill_"}
+
+
 def kernel_of(workload_name):
     if workload_name.startswith("decode_topk"):
         return "fused_topk"
@@ -570,8 +576,9 @@ def _pmc_avg(csv_dir, counter, name_part):
 
 def write_traffic_profile(workload_name, kernel_part, fetch_dir, write_dir, cal_fetch_dir,
                           cal_write_dir, cal_bytes, command):
-    fetch, nf = _pmc_avg(fetch_dir, "FETCH_SIZE", kernel_part)
-    write, nw_ = _pmc_avg(write_dir, "WRITE_SIZE", kernel_part)
+    name_part = KERNEL_NAME_PART.get(kernel_part, kernel_part)
+    fetch, nf = _pmc_avg(fetch_dir, "FETCH_SIZE", name_part)
+    write, nw_ = _pmc_avg(write_dir, "WRITE_SIZE", name_part)
     cfetch, _ = _pmc_avg(cal_fetch_dir, "FETCH_SIZE", "copyBuffer")
     cwrite, _ = _pmc_avg(cal_write_dir, "WRITE_SIZE", "copyBuffer")
     fetch_factor = cal_bytes / (cfetch * 1024)
@@ -652,7 +659,7 @@ def write_counter_profile(workload_name, kernel_part, dirs, command):
     --pmc runs, and what they say about the MFMA and VALU pipes."""
     avg, durations = {}, []
     for d in dirs:
-        disp = _pmc_dispatches(d, kernel_part)
+        disp = _pmc_dispatches(d, KERNEL_NAME_PART.get(kernel_part, kernel_part))
         if not disp:
             raise SystemExit("no samples for %r under %s" % (kernel_part, d))
         durations += [v["ns"] for v in disp.values()]
