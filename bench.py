@@ -769,8 +769,8 @@ def main():
 
     tun = parse_tunables(args.tunables)
     order = [args.only] if args.only is not None else [args.workload] + \
-        [i for i in (1, 22, 4, 3, 0, 5, 6, 23, 24, 16, 17, 7, 8, 9, 10, 11, 12, 13, 14, 15, 18,
-                     19, 20, 21) if i != args.workload]
+        [i for i in (1, 22, 4, 3, 0, 5, 6, 23, 24, 16, 17, 7, 8, 9, 10, 11, 12, 13, 25, 14, 15,
+                     18, 19, 20, 21) if i != args.workload]
     results, head, cpu = {}, None, {}
     for idx in order:
         wl = make_workload(idx, args.hot, tun)

@@ -57,11 +57,11 @@ extern "C" {
  *     ring_depth   1 = every wave streams its own K into registers; 2..7 =
  *                  a workgroup of 4 waves shares each K step through an LDS
  *                  ring of that many steps (head_dim 128 only: 32 heads with
- *                  4 rows per wave, 64 heads with 2 rows and depth 3 or 4;
- *                  the default there, at depth 4, for all but small
- *                  problems); 0 = the heuristic
- *     block_m      query rows per wave: 1, 2, 4 or 8 (with the ring 4 at 32
- *                  heads, 2 at 64)
+ *                  4 rows per wave, 64 heads with 2 rows and 128 heads with
+ *                  1 row at depth 3 or 4; the default at head_dim 128, at
+ *                  depth 4, for all but small problems); 0 = the heuristic
+ *     block_m      query rows per wave: 1, 2, 4 or 8 (with the ring 4, 2 or
+ *                  1 at 32, 64 or 128 heads)
  *     split_n      workgroups per row block along the columns, >= 1
  *     num_warps    waves per workgroup, 1..4: they split the column range
  *                  (4 with the ring, where they split the rows instead)

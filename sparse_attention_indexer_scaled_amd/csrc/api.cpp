@@ -147,15 +147,14 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
         return fail(MQA_ERR_INVALID_ARG, "prefill ring_depth must be 0, 1 (per-wave K) or 2..7 "
                     "(got %d)", t.ring_depth);
     // the shared-K ring: 4 waves of 4 rows at 32 heads (depth 2..7), of 2 rows
-    // at 64 heads (depth 3 or 4), head dim 128
-    const int ring_rows = num_heads == 32 ? 4 : 2;
+    // at 64 heads and of 1 row at 128 heads (depth 3 or 4), head dim 128
+    const int ring_rows = num_heads == 32 ? 4 : num_heads == 64 ? 2 : 1;
     if (t.ring_depth >= 2 &&
-        (head_dim != 128 || (num_heads != 32 && num_heads != 64) ||
-         (num_heads == 64 && t.ring_depth > 4) || (t.block_m != 0 && t.block_m != ring_rows) ||
-         (t.num_warps != 0 && t.num_warps != 4)))
+        (head_dim != 128 || (num_heads != 32 && t.ring_depth > 4) ||
+         (t.block_m != 0 && t.block_m != ring_rows) || (t.num_warps != 0 && t.num_warps != 4)))
         return fail(MQA_ERR_INVALID_ARG, "the shared-K prefill runs head_dim 128 with num_warps 4 "
                     "(or 0): 32 heads with ring_depth 2..7 and block_m 4, 64 heads with ring_depth "
-                    "3 or 4 and block_m 2");
+                    "3 or 4 and block_m 2, 128 heads with ring_depth 3 or 4 and block_m 1");
     if (M == 0 || N == 0)
         return ok();
     if (!q_fp8 || !k_fp8 || !kv_scale || !weights || !cu_seqlen_ks || !cu_seqlen_ke || !logits)
@@ -196,14 +195,13 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     p.head_dim = head_dim;
     const int64_t steps = ceil_div(N, 64);
     const bool small = M < 1024 && (int64_t)M * steps <= 16384;
-    // The shared-K ring (4 waves of 4 rows at 32 heads, of 2 rows at 64 heads;
-    // K through LDS) at head dim 128 for all but the small problems, unless
-    // the tunables ask otherwise: M 4096, N 32768 went from 508.3 to 447.6 us
-    // at 32 heads and from 1023.6 to 903.4 us at 64 (one MI355X, medians of
-    // three rounds).  At head dim 64 the per-wave kernel stays (319.8 against
-    // 322.9 us with the ring at its best split); 128 heads keep it too.
-    const bool ring_default = (num_heads == 32 || num_heads == 64) && head_dim == 128 && !small &&
-                              t.block_m == 0 && t.num_warps == 0;
+    // The shared-K ring (4 waves of 4, 2 or 1 rows at 32, 64 or 128 heads; K
+    // through LDS) at head dim 128 for all but the small problems, unless the
+    // tunables ask otherwise: M 4096, N 32768 went from 508.3 to 447.6 us at 32
+    // heads, from 1023.6 to 903.4 us at 64 and from 1793.8 to 1608.1 us at 128
+    // (one MI355X, medians of three rounds).  At head dim 64 the per-wave
+    // kernel stays (319.8 against 322.9 us with the ring at its best split).
+    const bool ring_default = head_dim == 128 && !small && t.block_m == 0 && t.num_warps == 0;
     p.ring = t.ring_depth >= 2 ? t.ring_depth : (t.ring_depth == 0 && ring_default ? 4 : 0);
     p.block_m = p.ring ? ring_rows : t.block_m ? t.block_m : (small ? 1 : std::min(4, max_block_m));
     p.num_warps = p.ring ? 4 : t.num_warps ? t.num_warps : (M >= 1024 || small ? 1 : 4);
@@ -211,11 +209,13 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     if (t.split_n) {
         p.split_n = t.split_n;
     } else if (p.ring) {
-        // ~1024 workgroups (two 4-wave workgroups per CU are resident), each
-        // walking at least 8 steps: split 4 on M 4096, N 32768 took 447.6 us
-        // against 450.1 with 2 and 451.4 with 8; ring depth 4 against 5 and 6
-        // level, 3 slower (one MI355X, medians of three rounds)
-        int64_t want = std::max<int64_t>(1, ceil_div(1024, nrb));
+        // ~1024 workgroups (two 4-wave workgroups per CU are resident) and at
+        // least 2 column parts, each walking at least 8 steps: on M 4096,
+        // N 32768 split 4 took 447.6 us against 450.1 with 2 and 451.4 with 8
+        // at 32 heads, split 2 903.4 against 902.7 with 4 at 64 heads, and
+        // 1608.1 against 1628.8 with 1 at 128 heads; ring depth 4 against 5
+        // and 6 level, 3 slower (one MI355X, medians of three rounds)
+        int64_t want = std::max<int64_t>(2, ceil_div(1024, nrb));
         int64_t cap = std::max<int64_t>(1, steps / 8);
         p.split_n = (int)std::min(want, cap);
     } else {

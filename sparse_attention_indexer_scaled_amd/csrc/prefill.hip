@@ -480,6 +480,13 @@ hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream)
             default: return hipErrorInvalidValue;
             }
         }
+        if (p.head_tiles == 4 && p.block_m == 1) {  // 128 heads: 1 row per wave
+            switch (p.ring) {
+            case 3: return launch_ring<1, 4, 4, 3, 128>(p, a, grid, stream);
+            case 4: return launch_ring<1, 4, 4, 4, 128>(p, a, grid, stream);
+            default: return hipErrorInvalidValue;
+            }
+        }
         if (p.head_tiles != 1 || p.block_m != 4)
             return hipErrorInvalidValue;
         switch (p.ring) {

@@ -346,6 +346,8 @@ CONFIGS = {
     # compute per byte (the shape of the issue page's ~5.4 TB/s figure)
     22: dict(kind="decode", name="decode_B16_nn1_ctx131072", B=16, next_n=1, ctx=131072,
              mml=131072),
+    # the long prefill chunk with 128 index heads
+    25: dict(kind="prefill", name="prefill_M4096_N32768_h128", M=4096, N=32768, H=128),
 }
 
 

@@ -122,12 +122,14 @@ def test_prefill_validation(lib):
     bad = _native.Tunables(num_warps=9)
     assert _prefill(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
     # the shared-K ring (1 = per-wave K): head dim 128, num_warps 4; 32 heads
-    # with depth 2..7 and block_m 4, 64 heads with depth 3 or 4 and block_m 2
+    # with depth 2..7 and block_m 4, 64 (128) heads with depth 3 or 4 and
+    # block_m 2 (1)
     for depth in (-1, 8):
         bad = _native.Tunables(ring_depth=depth)
         assert _prefill(lib, nulls, tun=ctypes.byref(bad)) == mqa._native.MQA_ERR_INVALID_ARG
         assert "ring_depth" in mqa.last_error()
-    for kw, shape in ((dict(ring_depth=4), dict(H=128)), (dict(ring_depth=4), dict(D=64)),
+    for kw, shape in ((dict(ring_depth=5), dict(H=128)), (dict(ring_depth=4, block_m=2), dict(H=128)),
+                      (dict(ring_depth=4), dict(D=64)),
                       (dict(ring_depth=5), dict(H=64)), (dict(ring_depth=4, block_m=4), dict(H=64)),
                       (dict(ring_depth=2, block_m=2), {}),
                       (dict(ring_depth=7, num_warps=1), {})):
@@ -137,7 +139,8 @@ def test_prefill_validation(lib):
         assert "shared-K" in mqa.last_error()
     for kw, shape in ((dict(ring_depth=1), {}), (dict(ring_depth=2), {}),
                       (dict(ring_depth=7, block_m=4, num_warps=4), {}),
-                      (dict(ring_depth=3, block_m=2), dict(H=64)), (dict(ring_depth=4), dict(H=64))):
+                      (dict(ring_depth=3, block_m=2), dict(H=64)), (dict(ring_depth=4), dict(H=64)),
+                      (dict(ring_depth=4), dict(H=128)), (dict(ring_depth=3, block_m=1), dict(H=128))):
         ok = _native.Tunables(**kw)  # valid: fails only on the NULL pointers
         assert _prefill(lib, nulls, tun=ctypes.byref(ok), **shape) == \
             mqa._native.MQA_ERR_INVALID_ARG

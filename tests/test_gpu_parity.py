@@ -273,15 +273,16 @@ def test_prefill_ring_equals_per_wave_kernel(mode):
             assert np.array_equal(run_prefill(p, clean=clean, tun=tun), want, equal_nan=True)
 
 
+@pytest.mark.parametrize("H", [64, 128])
 @pytest.mark.parametrize("mode", ["causal", "multi_req", "empty"])
-def test_prefill_ring_64_heads_equals_per_wave_kernel(mode):
-    """The 64-head shared-K ring (4 waves of 2 rows) against the per-wave
-    kernel, bit for bit."""
-    p = inputs.make_prefill(1000, 3000, seed=406, H=64, windows=mode)
+def test_prefill_ring_64_and_128_heads_equals_per_wave_kernel(mode, H):
+    """The shared-K ring at 64 heads (4 waves of 2 rows) and 128 heads (4
+    waves of 1 row) against the per-wave kernel, bit for bit."""
+    p = inputs.make_prefill(1000, 3000, seed=406, H=H, windows=mode)
     for clean in (True, False):
         want = run_prefill(p, clean=clean, tun=Tunables(ring_depth=1))
         for tun in (None, Tunables(ring_depth=4), Tunables(ring_depth=3, split_n=5, reverse_rows=1)):
-            say("prefill ring 64 heads mode=%s clean=%d" % (mode, clean))
+            say("prefill ring %d heads mode=%s clean=%d" % (H, mode, clean))
             assert np.array_equal(run_prefill(p, clean=clean, tun=tun), want, equal_nan=True)
 
 

@@ -44,7 +44,7 @@ def _decode_window(d):
     return p <= bound[:, None]
 
 
-@pytest.mark.parametrize("idx", [0, 3, 13, 15])
+@pytest.mark.parametrize("idx", [0, 3, 13, 25, 15])
 def test_prefill_workload(idx):
     t0 = time.time()
     p = inputs.make_config(idx)
