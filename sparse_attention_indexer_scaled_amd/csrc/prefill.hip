@@ -5,19 +5,24 @@
 //   logits[m, n] = sum_h relu(<Q[m,h,:], K[n,:]>) * kv_scale[n] * weights[m,h]
 // for max(ks[m],0) <= n < min(ke[m],N), and -inf elsewhere when clean_logits.
 //
-// Work decomposition.  A workgroup owns one block of BM consecutive query rows
-// and one of `split` contiguous parts of that block's column range (both pages,
-// "Technical Details": a row block shares one K stream; a column split fills the
-// device when the row grid is small).  The column range is the union of the
-// rows' windows rounded out to 64-column steps; the waves of the workgroup take
-// interleaved steps of the part (waves split the tile range, not the rows, so
-// each wave keeps its own independent K stream in flight).  Each wave keeps
-// its BM rows' Q and weights in VGPRs and, per step, loads 64 K rows + scales
-// straight into VGPRs (no LDS; the whole K buffer is shared by every row block
-// and stays L2/MALL resident), runs D/64 fp8 MFMAs per (row, 32-token tile), the
-// in-lane relu.weight sum, one permlane32 swap + add per row pair, the
-// once-per-column kv_scale multiply, and a masked store.  With clean_logits the
+// Two kernels, one arithmetic (the same step_scores and stores, so the same
+// bits).  Both give a workgroup a block of consecutive query rows and one of
+// `split` contiguous parts of the block's column range (both pages, "Technical
+// Details": a row block shares one K stream; a column split fills the device
+// when the row grid is small); the column range is the union of the rows'
+// windows rounded out to 64-column steps.  Each wave keeps its rows' Q and
+// weights in VGPRs and per step runs D/64 fp8 MFMAs per (row, 32-token tile),
+// the in-lane relu.weight sum, one permlane32 swap + add per row pair, the
+// once-per-column kv_scale multiply and a masked store; with clean_logits the
 // same waves write -inf left and right of the column range.
+//
+//   prefill_kernel (per-wave K; head dim 64, small problems): a workgroup owns
+//     BM rows and its waves take interleaved steps of the part, each loading
+//     its steps' 64 K rows + scales straight into VGPRs one step ahead.
+//   prefill_ring_kernel (shared K; the default at head dim 128): a workgroup
+//     of 4 waves owns 4 BM rows, every wave walks every step for its own BM
+//     rows, and the step arrives once for all four through an LDS ring (see
+//     the shared-K section below).
 //
 // Row blocks are dispatched high-m first when the host asks (causal chunks:
 // the last rows have the longest windows, so starting them first keeps them
