@@ -44,11 +44,14 @@ def _int_prefill(M, N, seed):
     return p
 
 
-@pytest.mark.parametrize("block_m", [1, 2, 4, 8])
+@pytest.mark.parametrize("block_m", [1, 2, 4, 8, "ring"])
 def test_prefill_integer_inputs_bit_exact(block_m):
-    p = _int_prefill(21, 333, seed=block_m)
-    say("prefill int M=21 N=333 block_m=%d" % block_m)
-    out = run_prefill(p, tun=Tunables(block_m=block_m))
+    """Every rows-per-wave instantiation of the per-wave kernel, and the
+    shared-K ring ("ring")."""
+    p = _int_prefill(21, 333, seed=5 if block_m == "ring" else block_m)
+    say("prefill int M=21 N=333 block_m=%s" % block_m)
+    tun = Tunables(ring_depth=4) if block_m == "ring" else Tunables(block_m=block_m)
+    out = run_prefill(p, tun=tun)
     ref, _ = oracle_prefill(p)
     if not np.array_equal(out, ref):
         bad = np.argwhere(out != ref)
@@ -105,6 +108,25 @@ def test_prefill_matches_oracle(M, N, mode, clean):
         assert np.isnan(out[~win]).all(), "clean_logits=0 wrote outside the window"
         out_w = np.where(win, out, -np.inf)
         assert_parity(out_w, ref, mag, f"prefill_{M}x{N}_{mode}_noclean")
+
+
+@pytest.mark.parametrize("M,N,mode", PREFILL_CASES, ids=[f"{m}x{n}-{w}" for m, n, w in PREFILL_CASES])
+def test_prefill_ring_matches_oracle(M, N, mode):
+    """The shared-K ring forced on the same cases (the heuristic gives these
+    small problems the per-wave kernel): one workgroup for M = 1, waves
+    without rows, a single clamped step for N < 64."""
+    p = inputs.make_prefill(M, N, seed=100 + M + N, windows=mode)
+    ref, mag = oracle_prefill(p)
+    for clean in (True, False):
+        say("prefill ring M=%d N=%d mode=%s clean=%d" % (M, N, mode, clean))
+        out = run_prefill(p, clean=clean, tun=Tunables(ring_depth=4))
+        if clean:
+            assert_parity(out, ref, mag, f"prefill_ring_{M}x{N}_{mode}")
+        else:
+            win = np.isfinite(ref)
+            assert np.isnan(out[~win]).all(), "clean_logits=0 wrote outside the window"
+            assert_parity(np.where(win, out, -np.inf), ref, mag, f"prefill_ring_{M}x{N}_{mode}_noclean")
+        assert np.array_equal(out, run_prefill(p, clean=clean), equal_nan=True)
 
 
 DECODE_CASES = [
