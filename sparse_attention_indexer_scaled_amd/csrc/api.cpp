@@ -539,8 +539,9 @@ extern "C" int paged_mqa_topk_decode_noalloc(const uint8_t *q_fp8, const uint8_t
         if (int rc = scratch_of_current_device(&ws))
             return rc;
     }
-    // Nothing in the workspace has to start at zero: every word a kernel reads
-    // was written earlier in the same call.
+    // Nothing in the workspace has to start at zero: every word whose value a
+    // kernel uses was written earlier in the same call (the select also reads
+    // ahead into its segments and ignores what lies past their counts).
     return paged_mqa_topk_decode(q_fp8, kv_cache, weights, context_lens, block_tables, indices,
                                  batch, next_n, num_heads, head_dim, kv_block_size, kv_layout,
                                  num_blocks, max_blocks_per_seq, max_model_len, k, ws,
