@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="headline workload index")
     ap.add_argument("--only", type=int, default=None, help="measure just this workload")
     ap.add_argument("--hot", action="store_true", help="one input copy (MALL-warm)")
+    ap.add_argument("--pages-table", action="store_true",
+                    help="time the decode shapes of the fp8 paged MQA logits PR page's "
+                         "performance table beside that page's HIP kernel (context, not the "
+                         "benchmark line)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--tunables", default="",
@@ -730,6 +734,31 @@ def read_traffic(workload_name):
     return t["hbm_read_bytes"] + t["hbm_write_bytes"]
 
 
+def pages_table(args, tun):
+    """Our decode on the shapes of the PR page's table (ragged +/- 30 %
+    contexts, 32 heads; per-token and preshuffled 64-token blocks), timed as
+    the benchmark times its workloads, beside that page's HIP kernel: a markdown
+    table and one JSON line of the figures."""
+    import torch
+    from sparse_attention_indexer_scaled_amd import inputs
+    rows = []
+    print("| B | next_n | kv_len | block | ours us | page's HIP us | ratio |", flush=True)
+    print("|---|---|---|---|---|---|---|", flush=True)
+    for idx, (cfg, page_us) in inputs.PAGES_TABLE.items():
+        wl = make_workload(idx, False, tun)
+        ms, reps = time_workload(wl, args.steps, args.warmup, repeats=args.repeats)
+        us = ms * 1e3
+        kv_len = int(round((cfg["ctx_range"][0] + cfg["ctx_range"][1]) / 2.0))
+        rows.append(dict(workload=cfg["name"], us_per_call=round(us, 3), page_hip_us=page_us,
+                         essential_TBps=round(wl.bytes / (us * 1e-6) / 1e12, 4)))
+        print("| %d | %d | %d | %d | %.1f | %.1f | %.2fx |" % (
+            cfg["B"], cfg["next_n"], kv_len, cfg["block_size"], us, page_us, page_us / us),
+            flush=True)
+        del wl
+        torch.cuda.empty_cache()
+    print(json.dumps({"pages_table": rows}))
+
+
 def main():
     args = parse()
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -768,6 +797,9 @@ def main():
         return
 
     tun = parse_tunables(args.tunables)
+    if args.pages_table:
+        pages_table(args, tun)
+        return
     order = [args.only] if args.only is not None else [args.workload] + \
         [i for i in (1, 22, 4, 3, 0, 5, 6, 23, 24, 16, 17, 7, 8, 9, 10, 11, 12, 13, 25, 14, 15,
                      18, 19, 20, 21) if i != args.workload]

@@ -351,6 +351,40 @@ CONFIGS = {
 }
 
 
+def _pages_decode(B, next_n, kv_len, block_size):
+    """A decode shape of the fp8 paged MQA logits PR page's performance table
+    ("Test Result": 32 heads, head dim 128, ragged contexts): each context
+    drawn uniformly from kv_len +/- 30 %, max_model_len the largest possible
+    draw rounded up to 64 tokens; 64-token blocks preshuffled, as the table
+    has them.  Context figures only: those of another kernel."""
+    lo, hi = int(0.7 * kv_len), int(1.3 * kv_len)
+    return dict(kind="decode", name="pages_B%d_nn%d_L%d_bs%d" % (B, next_n, kv_len, block_size),
+                B=B, next_n=next_n, ctx=None, ctx_range=(lo, hi), mml=(hi + 63) // 64 * 64,
+                block_size=block_size, preshuffle=block_size == 64)
+
+
+# The shapes of that table with its HIP kernel's time in us: index ->
+# (workload, page's HIP us).
+PAGES_TABLE = {
+    30: (_pages_decode(1, 2, 32768, 1), 5.4),
+    31: (_pages_decode(1, 6, 131072, 1), 14.3),
+    32: (_pages_decode(4, 2, 32768, 1), 10.2),
+    33: (_pages_decode(4, 6, 131072, 1), 40.2),
+    34: (_pages_decode(16, 2, 32768, 1), 29.2),
+    35: (_pages_decode(16, 6, 32768, 1), 46.9),
+    36: (_pages_decode(16, 6, 131072, 1), 212.7),
+    37: (_pages_decode(64, 2, 131072, 1), 594.0),
+    38: (_pages_decode(64, 6, 131072, 1), 982.8),
+    39: (_pages_decode(1, 2, 32768, 64), 4.3),
+    40: (_pages_decode(4, 6, 131072, 64), 27.6),
+    41: (_pages_decode(16, 6, 32768, 64), 32.7),
+    42: (_pages_decode(16, 6, 131072, 64), 141.2),
+    43: (_pages_decode(64, 6, 8192, 64), 32.5),
+    44: (_pages_decode(64, 6, 131072, 64), 551.7),
+}
+CONFIGS.update({i: w for i, (w, _) in PAGES_TABLE.items()})
+
+
 def make_config(idx: int, poison: bool = False):
     """The named workloads, seed = 1000 + index."""
     c = CONFIGS[idx]
