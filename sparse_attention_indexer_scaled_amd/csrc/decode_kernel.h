@@ -212,19 +212,28 @@ __device__ __forceinline__ void request_step(lds_u8 *slot, StepBlocks<entries_pe
     }
 }
 
-// Per-token blocks (BS = 1, the plain co-packed layout): token p's 128 K
-// bytes and 4 scale bytes sit at 132 * table[p], so rows are only 4-byte
-// aligned and every token has its own table entry.  A step's 64 entries are
-// staged in LDS (one global->LDS dword load, by wave 0, well ahead: see the
-// kernel), each wave reads the entries its loads need, and K moves with
-// 4-byte global->LDS loads: dword load jj of chunk c writes LDS bytes
-// 1024 c + 256 jj + 4 i from lane i, i.e. byte 4 (i % 4) of granule
-// position 16 jj + i / 4, which holds granule q = position ^ 8 (c & 1): token
-// 8c + (i / 4) % 8, 16-byte granule 2 jj + ((i / 32) ^ (c & 1)).  At head dim
-// 64 (68-byte records, chunks of 16 unswizzled rows) the same byte holds
-// token 16c + i / 4, granule jj.  So each lane needs one entry per chunk, and
-// four loads move a chunk.
+// Per-token blocks (BS = 1, the plain co-packed layout): token p's DIM K
+// bytes and 4 scale bytes sit at (DIM + 4) * table[p], so records are only
+// 4-byte aligned and every token has its own table entry.  A step's 64 entries
+// are staged in LDS (one global->LDS dword load, by wave 0, well ahead: see the
+// kernel), each wave reads the entries its loads need, and K moves with 4-byte
+// global->LDS loads.  Their slot holds the step's K rows in row order (row r at
+// DIM r), each row's 16-byte granules swizzled: granule u of row r sits at
+// position u ^ f(r), f(r) = (r / 2) % 8 at head dim 128 and (r / 4) % 4 at 64,
+// so that a 16-lane pass of ds_read_b128 over 16 rows touches each group of 4
+// banks once (read_block_rows).  A dword load writes 256 contiguous LDS bytes,
+// i.e. 2 whole rows (4 at head dim 64): lane i of load jj of chunk c fills byte
+// 4 (i % 4) of position (i % L) / 4 of chunk row R jj + i / L (R = 2, L = 32;
+// R = 4, L = 16 at head dim 64), so each load reads 2 (4) whole records where a
+// granule-ordered slot would need 32-byte pieces of 8 (16), and four loads
+// move a chunk.
 constexpr int kTokLoadsPerChunk = 4;
+
+template <int DIM>
+__device__ __forceinline__ int row_swizzle(int row)
+{
+    return DIM == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
 
 __device__ __forceinline__ int32_t lds_read_i32(uint32_t addr)
 {
@@ -239,31 +248,42 @@ __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, c
 {
     constexpr int KC = k_chunks<DIM>();
     constexpr int J = (KC + G - 1) / G;
+    constexpr int R = 1024 / DIM / kTokLoadsPerChunk;  // rows per load
+    constexpr int L = 64 / R;  // lanes per row
+    static_assert(R * kTokLoadsPerChunk * DIM == 1024, "four loads move a 1 KiB chunk");
     const bool scales = G == 1 || g == G - 1;
-    int32_t ent[J];
+    // The lane's offsets are the same every step; formed here each time (an
+    // opaque copy of the lane id), they are not hoisted out of the kernel's
+    // loop into registers the waves need.
+    asm volatile("" : "+v"(lane));
+    int32_t ent[J][kTokLoadsPerChunk];
     int32_t ent_s = 0;
     // Inline asm reads, completed by an explicit wait: the compiler would
     // otherwise make them wait for every outstanding global->LDS load.
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int c = g + G * j;
-        const int tok = DIM == 128 ? 8 * c + ((lane >> 2) & 7) : 16 * c + (lane >> 2);
-        ent[j] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * tok) : 0;
+#pragma unroll
+        for (int jj = 0; jj < kTokLoadsPerChunk; ++jj) {
+            const int row = rows_per_chunk<DIM>() * c + R * jj + lane / L;
+            ent[j][jj] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * row) : 0;
+        }
     }
     if (scales)
         ent_s = lds_read_i32(entries + 4 * lane);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        asm volatile("" : "+v"(ent[j]));
         const int c = g + G * j;
         if (G * J == KC || c < KC) {
-            const uint8_t *src = cache + (int64_t)ent[j] * (DIM + 4) +
-                                 (DIM == 128 ? 16 * ((lane >> 5) ^ (c & 1)) : 0) + 4 * (lane & 3);
 #pragma unroll
-            for (int jj = 0; jj < kTokLoadsPerChunk; ++jj)
-                __builtin_amdgcn_global_load_lds(src + (DIM == 128 ? 32 : 16) * jj,
-                                                 slot + 1024 * c + 256 * jj, 4, 0, kStreamHint);
+            for (int jj = 0; jj < kTokLoadsPerChunk; ++jj) {
+                asm volatile("" : "+v"(ent[j][jj]));
+                const int row = rows_per_chunk<DIM>() * c + R * jj + lane / L;
+                const int u = ((lane % L) >> 2) ^ row_swizzle<DIM>(row);
+                const uint8_t *src = cache + (int64_t)ent[j][jj] * (DIM + 4) + 16 * u + 4 * (lane & 3);
+                __builtin_amdgcn_global_load_lds(src, slot + 1024 * c + 256 * jj, 4, 0, kStreamHint);
+            }
         }
     }
     if (scales) {
@@ -271,6 +291,30 @@ __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, c
         __builtin_amdgcn_global_load_lds(cache + (int64_t)ent_s * (DIM + 4) + DIM,
                                          slot + kStep * DIM, 4, 0, kStreamHint);
     }
+}
+
+// Read a per-token slot (rows in row order, granules swizzled: see
+// request_tokens) into the MFMA operand layout: lane (t, g') takes granules
+// u = 2j + g' of token 32 h + t, as read_block does from the other slots.
+// Completed by read_wait.
+template <int DIM>
+__device__ __forceinline__ void read_block_rows(KStepOf<DIM> &k, uint32_t slot, int lane)
+{
+    asm volatile("" : "+v"(lane));  // see request_tokens
+    const int t = lane & 31, gq = lane >> 5;
+    const uint32_t sa = slot + kStep * DIM + t * 4;
+    const int f = row_swizzle<DIM>(t);  // the same for row t and row 32 + t
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t rb = slot + (32 * h + t) * DIM;
+#pragma unroll
+        for (int j = 0; j < DIM / 32; ++j) {
+            const uint32_t a = rb + 16 * ((2 * j + gq) ^ f);
+            asm volatile("ds_read_b128 %0, %1" : "=v"(k.t[h].c[j]) : "v"(a));
+        }
+    }
+    asm volatile("ds_read_b32 %0, %1 offset:0" : "=v"(k.sc[0]) : "v"(sa));
+    asm volatile("ds_read_b32 %0, %1 offset:128" : "=v"(k.sc[1]) : "v"(sa));
 }
 
 
@@ -502,7 +546,10 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                 next = Gth::fetch(cache, table, min(st + D, st1 - 1), last_entry);
             }
             KStepOf<DIM> kb;
-            read_block<DIM>(kb, ring_addr + rd * SB, lane);
+            if constexpr (BS == 1)
+                read_block_rows<DIM>(kb, ring_addr + rd * SB, lane);
+            else
+                read_block<DIM>(kb, ring_addr + rd * SB, lane);
             if (st > st0)
                 store_step(st - 1, prev_tot);
             rd = (rd + 1 == D) ? 0 : rd + 1;
