@@ -365,17 +365,27 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
         constexpr int H = kHeads * HT;
         Operand<DIM> q[R][HT];
         Weights16 w[R][HT];
-        // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f)
-        // and the entries kept so far for it (each row belongs to one wave, and
-        // within it to one half of the lanes, so the count needs no atomics)
+        // kFilter: this lane's row threshold (as a float: key >= t <=> value >= f),
+        // where its row's entries go, and how many each row of the pair has kept
+        // so far (each row belongs to one wave, and within it to one half of the
+        // lanes, so the counts are wave-uniform and need no atomics)
         float fthr[NP];
-        int kept[NP];
+        uint64_t *ebase[NP];
+        int kept_lo[NP], kept_hi[NP];
+        // all ones in the upper half of the lanes (hmask) or the lower (lmask),
+        // opaque so that the compiler keeps the masking below as two ANDs
+        // instead of turning it into selects
+        uint32_t hmask = half ? ~0u : 0u, lmask = ~hmask;
+        asm volatile("" : "+v"(hmask), "+v"(lmask));
         if constexpr (MODE == kFilter) {
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                const uint32_t tk = a.threshold[row_base + min(2 * i + half, nrows - 1)];
+                const int rr = min(2 * i + half, nrows - 1);
+                const uint32_t tk = a.threshold[row_base + rr];
                 fthr[i] = tk == 0u ? __builtin_inff() : key_float(tk);
-                kept[i] = 0;
+                ebase[i] = a.entries + (row_base + rr) * a.ent_stride + st0 * kStep;
+                kept_lo[i] = 0;
+                kept_hi[i] = 0;
             }
         }
 #pragma unroll
@@ -402,6 +412,11 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
             ostore[i] = rr < nrows;
         }
         const bool clean = a.clean != 0;
+        // kFilter: the last column a lane's row may keep
+        int olast[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+            olast[i] = min(obound[i], mml - 1);
         auto store_step = [&](int step, const float (&tot)[2][NP]) {
             const int p0 = step * kStep;
             if constexpr (MODE == kSample) {
@@ -421,21 +436,33 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
                 return;
             }
             if constexpr (MODE == kFilter) {
-                const uint32_t lt = (1u << t) - 1u;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int p = p0 + h * kTile + t;
 #pragma unroll
                     for (int i = 0; i < NP; ++i) {
-                        const bool keep =
-                            ostore[i] && p <= obound[i] && p < mml && tot[h][i] >= fthr[i];
-                        const uint64_t bal = __ballot(keep);
+                        const float v = tot[h][i];
+                        // (bitwise: lane masks combined without branches)
+                        const bool keep = ostore[i] & (p <= olast[i]) & (v >= fthr[i]);
                         // lanes 0..31 hold row 2i, lanes 32..63 row 2i + 1
-                        const uint32_t mine = half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-                        if (keep)
-                            a.entries[(row_base + 2 * i + half) * a.ent_stride + st0 * kStep +
-                                      kept[i] + __popc(mine & lt)] = fused_entry(tot[h][i], p);
-                        kept[i] += __popc(mine);
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+                        const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+                        if (keep) {
+                            // this half's count so far plus its kept lanes below
+                            // this one (mbcnt_hi counts nothing in the lower half;
+                            // the mask keeps the lower half's bits from the upper)
+                            const uint32_t base =
+                                (uint32_t)kept_lo[i] + ((uint32_t)(kept_hi[i] - kept_lo[i]) & hmask);
+                            const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                                hi, __builtin_amdgcn_mbcnt_lo(lo & lmask, base));
+                            // a kept value is finite (v >= fthr >= -FLT_MAX): its
+                            // order key, with -0 made +0 by the addition
+                            const uint32_t u = __float_as_uint(v + 0.0f);
+                            const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+                            ebase[i][slot] = entry(key, p);
+                        }
+                        kept_lo[i] += __builtin_popcount(lo);
+                        kept_hi[i] += __builtin_popcount(hi);
                     }
                 }
                 return;
@@ -562,7 +589,7 @@ __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restric
 #pragma unroll
             for (int i = 0; i < NP; ++i)
                 if (ostore[i] && t == 0)
-                    a.counts[(row_base + 2 * i + half) * a.split + s] = kept[i];
+                    a.counts[(row_base + 2 * i + half) * a.split + s] = half ? kept_hi[i] : kept_lo[i];
         }
         // No global->LDS load may still be in flight once the workgroup ends
         // and its LDS goes to the next workgroup.
