@@ -15,8 +15,11 @@
  *     row-major, on the current HIP device.  fp8 arrays are passed as raw
  *     bytes (uint8_t).  Data pointers must be 16-byte aligned, int32 arrays
  *     4-byte aligned.
- *   - The library allocates no device memory and keeps no state between calls
- *     except the per-thread last-error string.
+ *   - The library allocates no device memory.  Between calls it keeps only the
+ *     per-thread last-error string, a per-device cache of the gfx950 check
+ *     and, for paged_mqa_topk_decode_noalloc, its static scratch array (part
+ *     of the loaded code object, not an allocation) and that array's
+ *     per-device address.
  *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).  A
  *     call returns before the kernel finishes; outputs are valid once the
  *     stream has been synchronised.

@@ -178,10 +178,11 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
     p.N = N;
     p.clean = clean_logits ? 1 : 0;
     // Heuristic (measured on MI355X; both pages, "Technical Details", make
-    // the row block, split and wave count host-chosen): 4 rows per wave share
-    // each K step, with one wave per workgroup for long chunks and 4 waves for
-    // short ones; and enough column splits for ~2048 workgroups while each
-    // wave keeps >= 4 steps.  4 rows (228 VGPRs, 2 waves per SIMD) measured
+    // the row block, split and wave count host-chosen).  The per-wave kernel
+    // (head dim 64, small problems, explicit block_m / num_warps): 4 rows per
+    // wave share each K step, with one wave per workgroup for long chunks and
+    // 4 waves for short ones; and enough column splits for ~2048 workgroups
+    // while each wave keeps >= 4 steps.  4 rows (228 VGPRs, 2 waves per SIMD) measured
     // faster than 8 rows (1 wave per SIMD) on the long chunk although K is
     // re-read from L2 twice as often: M 4096, N 32768 took 525 against 536 us
     // at head dim 128 and 356 against 384 us at head dim 64 (means of three

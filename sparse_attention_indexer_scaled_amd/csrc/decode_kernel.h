@@ -11,9 +11,10 @@
 // the split's 64-token steps (one cache block each) in order.  Its G waves are
 // row groups: wave g holds rows [g R, g R + R) of the sequence's next_n rows
 // (Q: DIM / 8 VGPR per row and head tile, head weights: 16 VGPR per row and
-// head tile, for the wave's whole life).  All rows of the sequence share ONE K stream (both pages, "Technical
-// Details": rows share one K stream; the next_n-tiling issue page asks for
-// next_n folded into the tile rather than into the program count):
+// head tile, for the wave's whole life).  All rows of the sequence share ONE
+// K stream (both pages, "Technical Details": rows share one K stream; the
+// next_n-tiling issue page asks for next_n folded into the tile rather than
+// into the program count):
 //
 //   - K and scales travel HBM -> LDS by direct loads (global_load_lds, no
 //     VGPRs) into a ring of D slots, each slot one 64-token step (64 DIM bytes
@@ -52,7 +53,6 @@
 
 namespace mqa {
 namespace {
-
 
 constexpr int kSampleChunks = kFusedSampleChunks;
 constexpr int kSampleSteps = kFusedSampleSteps;
@@ -94,7 +94,6 @@ struct DecodeArgs {
 // overflow), and stores their count.
 enum DecodeMode { kLogits = 0, kSample = 1, kFilter = 2 };
 
-
 // Cache-policy bits of the global->LDS loads: nt (non-temporal).  Every cache
 // byte is read once per call, so the loads are marked streaming; measured on
 // MI355X this is worth about 10% on the long-context decode.
@@ -102,8 +101,9 @@ constexpr int kStreamHint = 2;
 
 // Where the 64 tokens of one step come from in a cache of BS-token blocks,
 // and how they are requested into a ring slot.  The slot layout is the same
-// for every block size (see read_block): 8 x 1 KiB chunks of K rows, then the
-// 64 scales.  A global_load_lds instruction writes lane i's 16 bytes at
+// for every block size of 16 or more tokens (see read_block): 8 x 1 KiB
+// chunks of K rows, then the 64 scales (per-token blocks fill their slots in
+// row order instead: see request_tokens).  A global_load_lds instruction writes lane i's 16 bytes at
 // slot + 1024 c + 16 i, so the lane -> granule assignment decides the LDS
 // layout: position i of chunk c holds granule q = i ^ (8 (c & 1)) of the
 // chunk, where q = 8 u + tau is 16-byte granule u of token 8c + tau.  Odd
@@ -235,12 +235,55 @@ __device__ __forceinline__ int row_swizzle(int row)
     return DIM == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
 }
 
-__device__ __forceinline__ int32_t lds_read_i32(uint32_t addr)
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
+// The table entries a wave's per-token loads need: entries R rows apart
+// (R = rows per load) at each of J chunk addresses, two ds_read2_b32 per chunk,
+// and the step's scale entry at sa.  The entries become global addresses, so
+// the reads and their wait are one asm block: no register is read, reused or
+// copied before its value has landed.  (Plain LDS reads would wait for every
+// outstanding global->LDS load.)
+#define MQA_RD2(j)                                                                   \
+    "ds_read2_b32 %[a" #j "], %[c" #j "] offset0:0 offset1:%[r1]\n\t"               \
+    "ds_read2_b32 %[b" #j "], %[c" #j "] offset0:%[r2] offset1:%[r3]\n\t"
+#define MQA_OUT2(j) [a##j] "=&v"(e[j][0]), [b##j] "=&v"(e[j][1])
+#define MQA_IN1(j) [c##j] "v"(ca[j])
+#define MQA_TAIL "ds_read_b32 %[s], %[sa]\n\ts_waitcnt lgkmcnt(0)"
+#define MQA_CONST [s] "=&v"(es) : [sa] "v"(sa), [r1] "n"(R), [r2] "n"(2 * R), [r3] "n"(3 * R)
+template <int J, int R>
+__device__ __forceinline__ void read_entries(const uint32_t (&ca)[J], uint32_t sa,
+                                             i32x2 (&e)[J][2], int32_t &es)
 {
-    int32_t v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+    static_assert(J == 1 || J == 2 || J == 3 || J == 4 || J == 8, "chunks per wave");
+    if constexpr (J == 1)
+        asm volatile(MQA_RD2(0) MQA_TAIL : MQA_OUT2(0), MQA_CONST, MQA_IN1(0) : "memory");
+    else if constexpr (J == 2)
+        asm volatile(MQA_RD2(0) MQA_RD2(1) MQA_TAIL
+                     : MQA_OUT2(0), MQA_OUT2(1), MQA_CONST, MQA_IN1(0), MQA_IN1(1)
+                     : "memory");
+    else if constexpr (J == 3)
+        asm volatile(MQA_RD2(0) MQA_RD2(1) MQA_RD2(2) MQA_TAIL
+                     : MQA_OUT2(0), MQA_OUT2(1), MQA_OUT2(2), MQA_CONST, MQA_IN1(0), MQA_IN1(1),
+                       MQA_IN1(2)
+                     : "memory");
+    else if constexpr (J == 4)
+        asm volatile(MQA_RD2(0) MQA_RD2(1) MQA_RD2(2) MQA_RD2(3) MQA_TAIL
+                     : MQA_OUT2(0), MQA_OUT2(1), MQA_OUT2(2), MQA_OUT2(3), MQA_CONST, MQA_IN1(0),
+                       MQA_IN1(1), MQA_IN1(2), MQA_IN1(3)
+                     : "memory");
+    else
+        asm volatile(MQA_RD2(0) MQA_RD2(1) MQA_RD2(2) MQA_RD2(3) MQA_RD2(4) MQA_RD2(5)
+                         MQA_RD2(6) MQA_RD2(7) MQA_TAIL
+                     : MQA_OUT2(0), MQA_OUT2(1), MQA_OUT2(2), MQA_OUT2(3), MQA_OUT2(4),
+                       MQA_OUT2(5), MQA_OUT2(6), MQA_OUT2(7), MQA_CONST, MQA_IN1(0), MQA_IN1(1),
+                       MQA_IN1(2), MQA_IN1(3), MQA_IN1(4), MQA_IN1(5), MQA_IN1(6), MQA_IN1(7)
+                     : "memory");
 }
+#undef MQA_RD2
+#undef MQA_OUT2
+#undef MQA_IN1
+#undef MQA_TAIL
+#undef MQA_CONST
 
 template <int G, int DIM = kDim>
 __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, const uint8_t *cache,
@@ -251,46 +294,37 @@ __device__ __forceinline__ void request_tokens(lds_u8 *slot, uint32_t entries, c
     constexpr int R = 1024 / DIM / kTokLoadsPerChunk;  // rows per load
     constexpr int L = 64 / R;  // lanes per row
     static_assert(R * kTokLoadsPerChunk * DIM == 1024, "four loads move a 1 KiB chunk");
-    const bool scales = G == 1 || g == G - 1;
     // The lane's offsets are the same every step; formed here each time (an
     // opaque copy of the lane id), they are not hoisted out of the kernel's
     // loop into registers the waves need.
     asm volatile("" : "+v"(lane));
-    int32_t ent[J][kTokLoadsPerChunk];
-    int32_t ent_s = 0;
-    // Inline asm reads, completed by an explicit wait: the compiler would
-    // otherwise make them wait for every outstanding global->LDS load.
+    // chunk c's entries for load jj: rows TPC c + R jj + lane / L (a chunk
+    // index past the step, when G does not divide KC, rereads the last chunk's
+    // entries and issues no load)
+    uint32_t ca[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int c = g + G * j;
-#pragma unroll
-        for (int jj = 0; jj < kTokLoadsPerChunk; ++jj) {
-            const int row = rows_per_chunk<DIM>() * c + R * jj + lane / L;
-            ent[j][jj] = (G * J == KC || c < KC) ? lds_read_i32(entries + 4 * row) : 0;
-        }
-    }
-    if (scales)
-        ent_s = lds_read_i32(entries + 4 * lane);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int j = 0; j < J; ++j)
+        ca[j] = entries + 4 * (rows_per_chunk<DIM>() * min(g + G * j, KC - 1) + lane / L);
+    i32x2 ent[J][2];
+    int32_t ent_s;
+    read_entries<J, R>(ca, entries + 4 * lane, ent, ent_s);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int c = g + G * j;
         if (G * J == KC || c < KC) {
 #pragma unroll
             for (int jj = 0; jj < kTokLoadsPerChunk; ++jj) {
-                asm volatile("" : "+v"(ent[j][jj]));
                 const int row = rows_per_chunk<DIM>() * c + R * jj + lane / L;
                 const int u = ((lane % L) >> 2) ^ row_swizzle<DIM>(row);
-                const uint8_t *src = cache + (int64_t)ent[j][jj] * (DIM + 4) + 16 * u + 4 * (lane & 3);
+                const uint8_t *src = cache + (int64_t)ent[j][jj >> 1][jj & 1] * (DIM + 4) +
+                                     16 * u + 4 * (lane & 3);
                 __builtin_amdgcn_global_load_lds(src, slot + 1024 * c + 256 * jj, 4, 0, kStreamHint);
             }
         }
     }
-    if (scales) {
-        asm volatile("" : "+v"(ent_s));
+    if (G == 1 || g == G - 1)
         __builtin_amdgcn_global_load_lds(cache + (int64_t)ent_s * (DIM + 4) + DIM,
                                          slot + kStep * DIM, 4, 0, kStreamHint);
-    }
 }
 
 // Read a per-token slot (rows in row order, granules swizzled: see
@@ -316,9 +350,6 @@ __device__ __forceinline__ void read_block_rows(KStepOf<DIM> &k, uint32_t slot, 
     asm volatile("ds_read_b32 %0, %1 offset:0" : "=v"(k.sc[0]) : "v"(sa));
     asm volatile("ds_read_b32 %0, %1 offset:128" : "=v"(k.sc[1]) : "v"(sa));
 }
-
-
-
 
 template <int R, int G, int D, int BS, int HT, int MODE = kLogits, int DIM = kDim>
 __global__ __launch_bounds__(64 * G) void decode_kernel(const uint8_t *__restrict__ qbuf,
