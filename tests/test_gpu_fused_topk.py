@@ -252,3 +252,74 @@ def test_fused_other_layouts_rows_the_sample_misjudges(bs, H, pre, D):
     assert_same(got, unfused(d, 2048), "misjudged bs=%d H=%d" % (bs, H))
     assert np.array_equal(got[0, :1000], high)
     assert np.array_equal(got[1], np.arange(2048))
+
+
+def _signed_zero_rows(ctx, seed):
+    """Two rows whose top 2048 are 1000 logits of 64 and then zeros of both
+    signs.  Heads 0-15 see dims 0-63 of K, heads 16-31 dims 64-127 (Q = 1.0
+    there); their weights are +1/16 and -1/16.  A position whose K is 1.0 in
+    dims 0-63 has the sum +64, in dims 64-127 the sum -64; its scale is 1
+    (logit +-64) or 0 (logit +0.0 or -0.0).  Per row: 1000 at +64, 1500 at
+    +0.0, 1500 at -0.0, the rest at -64, at random positions."""
+    d = inputs.make_decode(2, 1, [ctx, ctx], ctx, seed=seed, poison=True)
+    bs, D = d.block_size, d.D
+    d.q[:] = 0
+    d.q[..., :16, :64] = 0x38
+    d.q[..., 16:, 64:] = 0x38
+    d.weights[:, :16] = np.float32(1 / 16)
+    d.weights[:, 16:] = np.float32(-1 / 16)
+    kview, sview = inputs.cache_views(d.kv_cache, bs, D)
+    kinds = {}
+    rng = np.random.default_rng(seed + 1)
+    for b in range(2):
+        kind = np.full(ctx, 3)  # 0: +64, 1: +0.0, 2: -0.0, 3: -64
+        perm = rng.permutation(ctx)
+        kind[perm[:1000]], kind[perm[1000:2500]], kind[perm[2500:4000]] = 0, 1, 2
+        p = np.arange(ctx)
+        blocks, slots = d.block_tables[b, p // bs], p % bs
+        upper = (kind >= 2)[:, None]
+        kview[blocks, slots] = np.where(np.arange(D)[None, :] < 64, np.where(upper, 0, 0x38),
+                                        np.where(upper, 0x38, 0)).astype(np.uint8)
+        sview[blocks, slots] = np.where((kind == 1) | (kind == 2), 0.0, 1.0).astype(np.float32)
+        kinds[b] = kind
+    return d, kinds
+
+
+def test_fused_keeps_zeros_of_both_signs_in_order():
+    """Kept entries of +0.0 and -0.0 rank as equal (by column) through the
+    filtering decode's keys, the sampled-threshold path of the select (no row
+    is recomputed: 4000 entries pass a threshold at zero)."""
+    ctx = 16384
+    d, kinds = _signed_zero_rows(ctx, seed=980)
+    dv = decode_device_inputs(d)
+    logits = run_decode(d, dv=dv)
+    for b in range(2):
+        zero = (kinds[b] == 1) | (kinds[b] == 2)
+        assert np.all(logits[b][kinds[b] == 0] == 64) and np.all(logits[b][zero] == 0)
+        assert np.all(np.signbit(logits[b][kinds[b] == 2]))
+        assert not np.any(np.signbit(logits[b][kinds[b] == 1]))
+    k = 2048
+    need = _native.paged_mqa_topk_workspace_size(d.B, d.next_n, d.max_model_len)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    out = torch.full((2, k), -7, dtype=torch.int32, device="cuda")
+    say("fused topk signed zeros k=%d" % k)
+    _native.paged_mqa_topk_decode(dv["q"], dv["cache"], dv["w"], dv["ctx"], dv["bt"],
+                                  d.max_model_len, k, kv_block_size=d.block_size, indices=out,
+                                  workspace=ws, preshuffle=d.preshuffle)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    # the workspace's per-row recompute flags (entries, counts, thresholds, flags;
+    # each region 256-byte aligned)
+    rows = 2
+    al = lambda n: (n + 255) // 256 * 256
+    ent_stride = (ctx + 63) // 64 * 64
+    off = al(rows * ent_stride * 8) + al(rows * 1024 * 4) + al(rows * 4)
+    flags = ws[off:off + rows * 4].view(torch.int32).cpu().numpy()
+    assert not flags.any(), "a row was recomputed: the filtered path was not taken"
+    assert_same(got, unfused(d, k, dv=dv), "signed zeros")
+    for b in range(2):
+        assert np.array_equal(got[b, :1000], np.sort(np.nonzero(kinds[b] == 0)[0]))
+        zeros = np.sort(np.nonzero((kinds[b] == 1) | (kinds[b] == 2))[0])[:k - 1000]
+        assert np.array_equal(got[b, 1000:], zeros)
+        picked = kinds[b][got[b, 1000:]]
+        assert (picked == 1).any() and (picked == 2).any()
