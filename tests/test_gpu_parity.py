@@ -217,6 +217,22 @@ def test_decode_other_block_sizes(bs, B, next_n, ctx, mml):
         assert_parity(out, ref, mag, f"decode_bs{bs}_B{B}_nn{next_n}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("next_n", [4, 5, 7, 8])
+def test_per_token_blocks_many_waves(next_n, D):
+    """Per-token blocks with one row per wave, so next_n waves split each
+    step's K chunks: 4-8 waves, where a wave requests one or two chunks and,
+    when the wave count does not divide the chunk count, the last chunks'
+    waves request one fewer."""
+    d = inputs.make_decode(2, next_n, [1500, 70], 1536, seed=335 + next_n + D, D=D, block_size=1,
+                           poison=True)
+    say("decode bs=1 D=%d next_n=%d rows_per_block=1" % (D, next_n))
+    ref, mag, _ = oracle_decode(d)
+    for tun in (Tunables(rows_per_block=1), Tunables(rows_per_block=1, split_kv=5)):
+        out = run_decode(d, tun=tun)
+        assert_parity(out, ref, mag, f"decode_bs1_D{D}_nn{next_n}_rows1")
+
+
 @pytest.mark.parametrize("bs", [1, 16, 128])
 def test_block_size_does_not_change_bits(bs):
     """The same tokens paged through 1-, 16- or 128-token blocks give the
