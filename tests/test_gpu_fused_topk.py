@@ -92,7 +92,7 @@ def test_fused_preshuffled_cache_and_tunables():
     dv = decode_device_inputs(d)
     want = unfused(d, 2048, dv=dv)
     for tun in (None, Tunables(split_kv=1), Tunables(rows_per_block=1, split_kv=37),
-                Tunables(rows_per_block=4, split_kv=300)):
+                Tunables(rows_per_block=3, split_kv=11), Tunables(rows_per_block=4, split_kv=300)):
         say("fused topk preshuffled tun=%s" % (None if tun is None else
                                                [getattr(tun, f) for f, _ in Tunables._fields_]))
         assert_same(fused(d, 2048, tun=tun, dv=dv), want, "preshuffled")
