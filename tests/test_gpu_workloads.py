@@ -64,7 +64,7 @@ def test_prefill_workload(idx):
     assert_parity(out[rows], ref, mag, f"workload{idx}")
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20, 21, 22])
+@pytest.mark.parametrize("idx", [1, 2, 4, 9, 10, 11, 12, 14, 18, 19, 20, 21, 22, 36, 42])
 def test_decode_workload(idx):
     t0 = time.time()
     d = inputs.make_config(idx, poison=True)
@@ -77,6 +77,8 @@ def test_decode_workload(idx):
     assert np.isfinite(out[win]).all()
     if idx == 4:
         seqs = [int(np.argmin(d.context_lens)), int(np.argmax(d.context_lens)), 17]
+    elif inputs.CONFIGS[idx]["ctx"] is None:  # ragged lengths: the shortest, the longest, one more
+        seqs = sorted({int(np.argmin(d.context_lens)), int(np.argmax(d.context_lens)), d.B // 2 + 1})
     elif idx == 2:
         seqs = list(range(d.B))  # the headline: every row
     else:
