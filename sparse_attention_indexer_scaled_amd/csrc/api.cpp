@@ -356,12 +356,15 @@ int prepare_decode(const uint8_t *q_fp8, const uint8_t *kv_cache, const float *w
                                       : std::max(ceil_div(1024, batch), ceil_div(steps_max, 32));
         const int64_t cap = std::max<int64_t>(1, short_ctx ? steps_max : steps_max / 2);
         int64_t split = std::max<int64_t>(1, std::min(want, cap));
-        // When the step cap binds (small batches of shorter contexts), the
-        // grid is rounded down to whole rounds of workgroups over the 256 CUs:
-        // an uneven last round leaves some CUs one workgroup more than the
-        // rest (B 1, next_n 2, 32768 tokens in per-token blocks: 333 -> 256
-        // workgroups, 6.64 -> 5.70 us on one MI355X).
-        if (want > cap && batch * split > 256)
+        // The grid is rounded down to whole rounds of workgroups over the 256
+        // CUs: a few workgroups past a multiple of 256 give some CUs one more
+        // than the others, and the call waits for those (with four resident
+        // per CU, the extra one runs as a second round).  Next_n 6, 131072
+        // tokens: B 6 split 171 (1026 workgroups) 39.09 us against 170 (1020)
+        // 30.96 us, B 12 86 against 85 67.14 / 53.30 us, B 3 22.39 / 19.30 us;
+        // where the step cap binds, B 1, next_n 2, 32768 tokens in per-token
+        // blocks 333 -> 256 workgroups, 6.64 -> 5.70 us (one MI355X).
+        if (!short_ctx && batch * split > 256)
             split = std::max<int64_t>(1, batch * split / 256 * 256 / batch);
         p.split_kv = (int)split;
     }
