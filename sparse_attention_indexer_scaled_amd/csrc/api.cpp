@@ -218,7 +218,18 @@ extern "C" int mqa_logits_prefill(const uint8_t *q_fp8, const uint8_t *k_fp8, co
         // and 6 level, 3 slower (one MI355X, medians of three rounds)
         int64_t want = std::max<int64_t>(2, ceil_div(1024, nrb));
         int64_t cap = std::max<int64_t>(1, steps / 8);
-        p.split_n = (int)std::min(want, cap);
+        int64_t split = std::min(want, cap);
+        // and the grid rounded down to whole rounds of 256 workgroups (as the
+        // decode's), keeping two parts: causal chunks of N 32768 with M 1000
+        // took 142.9 us at split 17 (1071 workgroups) against 129.0 at 16,
+        // M 3000 368.2 against 351.9 us (6 -> 5), and M 2500, N 16384 162.5
+        // against 151.3 us (7 -> 6), one MI355X
+        if (nrb * split > 256) {
+            const int64_t r = nrb * split / 256 * 256 / nrb;
+            if (r >= 2)
+                split = r;
+        }
+        p.split_n = (int)split;
     } else {
         // ~2048 workgroups; ~8192 at head dim 64 (split 8 on the long chunk: 355
         // against 366 us with split 2, three alternating runs on one MI355X)
